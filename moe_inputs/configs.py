@@ -1,0 +1,72 @@
+"""The five workload shapes of the MoE expert layer.
+
+Shapes follow the layer definition  out[t] = sum_j w[t,j] * W2[e] (SiLU(W13g[e] x_t) * W13u[e] x_t),
+e = ids[t,j], with X[T,H], W13[E,2I,H] (rows [0,I) gate, [I,2I) up) and W2[E,H,I]
+("factor_moe_fused_gemm.cu", header comment with the slow PyTorch path).
+"""
+from dataclasses import dataclass
+
+
+@dataclass(frozen=True)
+class MoEConfig:
+    name: str
+    T: int            # tokens
+    H: int            # hidden size
+    I: int            # expert intermediate size
+    E: int            # experts
+    top_k: int
+    w_dtype: str      # "f32" | "bf16" | "e4m3"  (expert weights)
+    x_dtype: str      # "f32" | "bf16"           (hidden states and layer output)
+    renormalize: bool  # routing weights renormalised to sum 1 over the chosen experts
+    logit_bias_std: float = 0.0  # per-expert router bias ~ N(0, std), skews expert loads
+    weight_std: float = 0.02
+    block: int = 128   # fp8: weight block edge and activation group width
+    description: str = ""
+
+    @property
+    def n_slots(self) -> int:
+        return self.T * self.top_k
+
+    @property
+    def useful_flops_up(self) -> int:
+        """Up projection alone: 2 * N * H * 2I = 4*T*k*H*I (padding rows excluded)."""
+        return 4 * self.T * self.top_k * self.H * self.I
+
+    @property
+    def useful_flops_layer(self) -> int:
+        """Both projections: 6*T*k*H*I."""
+        return 6 * self.T * self.top_k * self.H * self.I
+
+
+CONFIGS = {
+    c.name: c
+    for c in [
+        MoEConfig("tiny_fp32", T=16, H=128, I=256, E=8, top_k=2, w_dtype="f32", x_dtype="f32",
+                  renormalize=True,
+                  description="tiny fp32 layer, top-2 renormalised"),
+        MoEConfig("mixtral_prefill_bf16", T=4096, H=4096, I=14336, E=8, top_k=2, w_dtype="bf16",
+                  x_dtype="bf16", renormalize=True,
+                  description="Mixtral-8x7B-shaped prefill, bf16, top-2 renormalised"),
+        MoEConfig("dsv3_decode_bf16", T=64, H=7168, I=2048, E=256, top_k=8, w_dtype="bf16",
+                  x_dtype="bf16", renormalize=False,
+                  description="DeepSeek-V3-shaped decode batch, bf16, top-8"),
+        MoEConfig("skewed_prefill_bf16", T=8192, H=2048, I=1408, E=64, top_k=6, w_dtype="bf16",
+                  x_dtype="bf16", renormalize=False, logit_bias_std=2.0,
+                  description="skewed-routing prefill, bf16, top-6, router bias ~N(0,2)"),
+        MoEConfig("dsv3_fp8_e4m3", T=2048, H=7168, I=2048, E=256, top_k=8, w_dtype="e4m3",
+                  x_dtype="bf16", renormalize=False,
+                  description="fp8 e4m3 weights with 128x128 fp32 block scales, bf16 X "
+                              "quantised per token row in 128-wide groups, top-8"),
+    ]
+}
+
+# Order of the workloads as they are listed (the small fp32 case first).
+CONFIG_ORDER = ["tiny_fp32", "mixtral_prefill_bf16", "dsv3_decode_bf16",
+                "skewed_prefill_bf16", "dsv3_fp8_e4m3"]
+
+
+def get_config(name: str, **overrides) -> MoEConfig:
+    """Look up a workload by name; keyword overrides give a shrunk variant of it."""
+    from dataclasses import replace
+    base = CONFIGS[name]
+    return replace(base, **overrides) if overrides else base

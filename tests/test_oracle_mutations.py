@@ -1,0 +1,114 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check that a pin catches each.
+
+Each mutant replaces one oracle function with a subtly wrong copy; the pins in
+test_oracle_layer / test_oracle_align must then fail.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import moe_oracle as mo
+import test_oracle_align as ta
+import test_oracle_layer as tl
+
+
+def _up_swapped(x_rows, w13_e):
+    x_rows = np.asarray(x_rows, np.float64)
+    I = w13_e.shape[0] // 2
+    return mo.silu(x_rows @ w13_e[I:].T) * (x_rows @ w13_e[:I].T)
+
+
+def _up_wrong_silu(x_rows, w13_e):
+    x_rows = np.asarray(x_rows, np.float64)
+    I = w13_e.shape[0] // 2
+    g = x_rows @ w13_e[:I].T
+    return g / (1.0 + np.exp(g)) * (x_rows @ w13_e[I:].T)
+
+
+def _down_transposed(act, w2_e):
+    w = np.asarray(w2_e, np.float64)
+    return np.asarray(act, np.float64) @ w.reshape(w.shape[1], w.shape[0])
+
+
+def _combine_drops_last(slot_out, top_k, acc_dtype=np.float64):
+    y = np.asarray(slot_out)
+    T = y.shape[0] // top_k
+    acc = np.zeros((T, y.shape[1]), acc_dtype)
+    for j in range(max(top_k - 1, 1)):
+        acc = acc + y[j::top_k]
+    return acc
+
+
+LAYER_MUTANTS = {
+    "gate_up_swapped": ("expert_up", _up_swapped),
+    "silu_sign": ("expert_up", _up_wrong_silu),
+    "w2_transposed_layout": ("expert_down", _down_transposed),
+    "combine_drops_slot": ("combine", _combine_drops_last),
+}
+
+LAYER_PINS = [tl.test_closed_form_worked_example,
+              lambda: tl.test_dense_reduction_top1_weight1(5),
+              tl.test_top_k_equals_E_mean_of_experts,
+              tl.test_weighted_sum_of_dense_mlps]
+
+
+def _some_pin_fails(pins):
+    for pin in pins:
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            return True
+    return False
+
+
+@pytest.mark.parametrize("name", list(LAYER_MUTANTS))
+def test_layer_mutant_is_caught(name, monkeypatch):
+    attr, fn = LAYER_MUTANTS[name]
+    monkeypatch.setattr(mo, attr, fn)
+    assert _some_pin_fails(LAYER_PINS), f"no pin caught mutant {name}"
+
+
+def _gather_token_mod(x, topk_ids, topk_weights, experts, num_experts=None, **kw):
+    # wrong gather: token = slot % k instead of slot // k
+    ids = np.asarray(topk_ids)
+    T, k = ids.shape
+    x = np.asarray(x, np.float64)
+    idx = [(t * k + j) % T for t in range(T) for j in range(k)]
+    return _ORIG_LAYER(x[np.array(idx[::k])], topk_ids, topk_weights, experts, num_experts, **kw)
+
+
+_ORIG_LAYER = mo.moe_layer
+
+
+def test_wrong_gather_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "moe_layer", _gather_token_mod)
+    assert _some_pin_fails([tl.test_permutation_equivariance, tl.test_closed_form_worked_example])
+
+
+def _align_unstable(topk_ids, num_experts, block_m):
+    a = _ORIG_ALIGN(topk_ids, num_experts, block_m)
+    # reverse each expert's segment (a non-stable order)
+    for e in range(num_experts):
+        lo, n = a.offsets[e], a.counts[e]
+        seg = a.sorted_slots[lo:lo + n][::-1].copy()
+        a.sorted_slots[lo:lo + n] = seg
+        a.slot_row[seg] = np.arange(lo, lo + n)
+    return a
+
+
+def _align_no_padding(topk_ids, num_experts, block_m):
+    a = _ORIG_ALIGN(topk_ids, num_experts, 1)
+    return a
+
+
+_ORIG_ALIGN = mo.align
+
+
+@pytest.mark.parametrize("mutant", [_align_unstable, _align_no_padding])
+def test_align_mutant_is_caught(mutant, monkeypatch):
+    monkeypatch.setattr(oracle, "align", mutant)
+    import json
+    cases = json.load(open(ta.GOLDEN))["cases"]
+    pins = [lambda c=c: ta.test_align_worked_examples(c) for c in cases]
+    pins += [lambda: ta.test_align_matches_brute_force(*next(iter(ta.adversarial_routings())))]
+    assert _some_pin_fails(pins)
