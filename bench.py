@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed grouped-GEMM top-k MoE expert layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-baseline on|off]
+
+A step is one pass of the whole layer over one batch of synthetic input already
+resident in HBM: moe_align -> [moe_quantize_rows_e4m3] -> moe_grouped_gemm_up ->
+moe_grouped_gemm_down -> moe_combine, each through the C ABI on the current stream
+(the same kernels, launch shapes and order moe_forward uses; moe_forward itself is
+timed as well and reported as ms_per_step_forward).  HIP events between the
+stages give each kernel's average duration over the timed steps.
+
+Default workload: Mixtral-8x7B-shaped prefill (T=4096, H=4096, I=14336, E=8,
+top-2, bf16).  Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused MoE layer useful TFLOP/s + % MFMA peak (prefill), HBM GB/s (decode)"
+PEAK_TFLOPS = {"bf16": 2516.6, "e4m3": 5033.2, "f32": 157.3}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "mixtral_prefill_bf16"
+CPU_SAMPLE_TOKENS = {"tiny_fp32": 16, "mixtral_prefill_bf16": 256, "dsv3_decode_bf16": 8,
+                     "skewed_prefill_bf16": 256, "dsv3_fp8_e4m3": 16}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(cfg, ids, bm, rows_max, tiles_max):
+    """Per-kernel algorithmic flops and HBM bytes of one launch (padding excluded)."""
+    import numpy as np
+    N, T, H, I, E = cfg.T * cfg.top_k, cfg.T, cfg.H, cfg.I, cfg.E
+    active = int((np.bincount(ids.reshape(-1), minlength=E)[:E] > 0).sum())
+    fp8 = cfg.w_dtype == "e4m3"
+    xe = 4 if cfg.x_dtype == "f32" else 2
+    we = {"f32": 4, "bf16": 2, "e4m3": 1}[cfg.w_dtype]
+    ae = 1 if fp8 else xe
+    x_in = 1 if fp8 else xe
+    sc = (lambda r, c: 4 * r * (c // 128)) if fp8 else (lambda r, c: 0)
+    wsc = (lambda r, c: 4 * (r // 128) * (c // 128)) if fp8 else (lambda r, c: 0)
+    work = {
+        "align": dict(flops=0, bytes=4 * N + 4 * E + 4 * (E + 1) + 4 * rows_max + 4 * N + 8 * tiles_max + 8),
+        "up": dict(flops=4 * N * H * I,
+                   bytes=N * H * x_in + sc(N, H) + active * (2 * I * H * we + wsc(2 * I, H))
+                   + N * I * ae + sc(N, I)),
+        "down": dict(flops=2 * N * H * I,
+                     bytes=N * I * ae + sc(N, I) + active * (H * I * we + wsc(H, I)) + N * H * xe + 4 * N),
+        "combine": dict(flops=0, bytes=N * H * xe + T * H * xe + 4 * N),
+    }
+    if fp8:
+        work["quant"] = dict(flops=0, bytes=T * H * 2 + T * H + sc(T, H))
+    return work, active
+
+
+def cpu_baseline(case, n_tokens):
+    """Time the CPU oracle (as it stands) on the first n_tokens tokens of the workload."""
+    import numpy as np
+
+    import oracle
+    cfg = case.cfg
+    toks = list(range(min(n_tokens, cfg.T)))
+    needed = sorted(set(int(e) for e in case.ids_host[toks].reshape(-1)))
+    log(f"cpu_baseline: fetching {len(needed)} experts to the host")
+    host = {e: case.expert_host(e) for e in needed}
+    x = case.x_host()
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    log(f"cpu_baseline: oracle on {len(toks)} tokens ({threads} BLAS threads)")
+    t0 = time.perf_counter()
+    oracle.moe_layer(x, case.ids_host, case.w_host, lambda e: host[e], cfg.E,
+                     fp8=cfg.w_dtype == "e4m3", tokens=toks)
+    dt = time.perf_counter() - t0
+    flops = 4 * len(toks) * cfg.top_k * cfg.H * cfg.I
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"first {len(toks)} of {cfg.T} tokens of {cfg.name} (all their experts), "
+                      f"float64 numpy oracle, weights prefetched to host; useful flops 4*n*k*H*I"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--block-m", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this layer runs on one GPU only (no sharding, no collectives); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import routed_grouped_gemm_topk_amd as moe
+    from moe_inputs import CONFIGS, make_case, routing_stats
+
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"generating {cfg.name} on {torch.cuda.get_device_name(dev)}")
+    case = make_case(cfg, dev, seed=0)
+    p = moe.make_problem(cfg.T, cfg.H, cfg.I, cfg.E, cfg.top_k, cfg.x_dtype, cfg.w_dtype, args.block_m)
+    bm = moe.moe_pick_block_m(p)
+    rows, mt = moe.moe_max_padded_slots(p), moe.moe_max_tiles(p)
+    fp8 = cfg.w_dtype == "e4m3"
+    a = moe.alloc_align(p, dev)
+    act = torch.empty((rows, cfg.I), dtype=torch.uint8 if fp8 else case.x.dtype, device=dev)
+    act_scales = torch.empty((rows, cfg.I // 128), dtype=torch.float32, device=dev) if fp8 else None
+    xq = torch.empty((cfg.T, cfg.H), dtype=torch.uint8, device=dev) if fp8 else None
+    x_scales = torch.empty((cfg.T, cfg.H // 128), dtype=torch.float32, device=dev) if fp8 else None
+    slot_out = torch.empty((cfg.T * cfg.top_k, cfg.H), dtype=case.x.dtype, device=dev)
+    out = torch.empty((cfg.T, cfg.H), dtype=case.x.dtype, device=dev)
+    ws = moe.alloc_workspace(p, dev)
+    stages = ["align"] + (["quant"] if fp8 else []) + ["up", "down", "combine"]
+
+    def step(evs=None):
+        i = 0
+
+        def mark():
+            nonlocal i
+            if evs is not None:
+                evs[i].record()
+            i += 1
+        mark()
+        moe.moe_align(p, case.topk_ids, a["counts"], a["offsets"], a["sorted_slots"], a["slot_row"],
+                      a["tiles"], a["num_tiles"], a["n_invalid"])
+        mark()
+        x_in = case.x
+        if fp8:
+            moe.moe_quantize_rows_e4m3(p, case.x, xq, x_scales)
+            x_in = xq
+            mark()
+        moe.moe_grouped_gemm_up(p, x_in, x_scales, case.w13, case.w13_scales, a["sorted_slots"],
+                                a["tiles"], a["num_tiles"], act, act_scales)
+        mark()
+        moe.moe_grouped_gemm_down(p, act, act_scales, case.w2, case.w2_scales, case.topk_weights,
+                                  a["sorted_slots"], a["tiles"], a["num_tiles"], slot_out)
+        mark()
+        moe.moe_combine(p, slot_out, a["slot_row"], out)
+        mark()
+
+    log(f"warmup {args.warmup} steps (block_m={bm}, tiles<= {mt})")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = {s: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+               for i, s in enumerate(stages)}
+    log(f"staged step {ms_per_step:.4f} ms; kernels " + ", ".join(f"{k} {v:.4f}" for k, v in kern_ms.items()))
+
+    # moe_forward on its own (one entry point, same kernels)
+    for _ in range(3):
+        moe.forward(p, case.x, case.topk_ids, case.topk_weights, case.w13, case.w2, case.w13_scales,
+                    case.w2_scales, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        moe.forward(p, case.x, case.topk_ids, case.topk_weights, case.w13, case.w2, case.w13_scales,
+                    case.w2_scales, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    ms_forward = (time.perf_counter() - t2) * 1e3 / args.steps
+
+    work, active = algorithmic_work(cfg, case.ids_host, bm, rows, mt)
+    layer_flops_4 = cfg.useful_flops_up
+    layer_flops_6 = cfg.useful_flops_layer
+    layer_bytes = sum(w["bytes"] for w in work.values())
+    wdt = cfg.w_dtype if cfg.w_dtype != "f32" else "f32"
+    peak_tf = PEAK_TFLOPS[wdt]
+    ridge = peak_tf * 1e12 / (PEAK_HBM_GBS * 1e9)
+    hbm_bound_layer = layer_flops_6 / layer_bytes < ridge
+
+    dom = max(("up", "down"), key=lambda s: kern_ms[s])
+    dw = work[dom]
+    dom_s = kern_ms[dom] * 1e-3
+    if dw["flops"] / dw["bytes"] >= ridge:
+        roof = {"kernel": f"moe_grouped_gemm_{dom}", "bound": "mfma",
+                "achieved": dw["flops"] / dom_s / 1e12, "peak": peak_tf, "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": f"moe_grouped_gemm_{dom}", "bound": "hbm",
+                "achieved": dw["bytes"] / dom_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["algorithmic_per_launch"] = {"flops": dw["flops"], "bytes": dw["bytes"]}
+    roof["avg_launch_ms"] = kern_ms[dom]
+
+    if hbm_bound_layer:
+        value, unit = layer_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s"
+    else:
+        value, unit = layer_flops_4 / (ms_per_step * 1e-3) / 1e12, "TFLOP/s"
+
+    per_kernel = {}
+    for s in stages:
+        t = kern_ms[s] * 1e-3
+        d = {"ms": round(kern_ms[s], 5), "GB/s": round(work[s]["bytes"] / t / 1e9, 1)}
+        if work[s]["flops"]:
+            d["TFLOP/s"] = round(work[s]["flops"] / t / 1e12, 1)
+            d["pct_mfma_peak"] = round(100 * work[s]["flops"] / t / 1e12 / peak_tf, 2)
+        d["pct_hbm_peak"] = round(100 * work[s]["bytes"] / t / 1e9 / PEAK_HBM_GBS, 2)
+        per_kernel[s] = d
+
+    cpu = None
+    if args.cpu_baseline == "on":
+        cpu = cpu_baseline(case, CPU_SAMPLE_TOKENS.get(cfg.name, 64))
+        if unit == "GB/s":
+            cpu["note"] = "reported in TFLOP/s (useful flops); the GPU value is GB/s"
+
+    st = routing_stats(case.ids_host, cfg.E)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_forward": round(ms_forward, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "e4m3": "e4m3xe4m3->f32 (bf16 io)"}[cfg.w_dtype],
+        "data": "synthetic (seeded N(0,1) X, N(0,0.02) weights, softmax top-k routing)",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
+                   "top_k": cfg.top_k, "block_m": bm, "active_experts": active,
+                   "max_per_expert": st["max_per_expert"], "parallelism": "single GPU"},
+        "useful_tflops_4tkhi": round(layer_flops_4 / (ms_per_step * 1e-3) / 1e12, 2),
+        "layer_tflops_6tkhi": round(layer_flops_6 / (ms_per_step * 1e-3) / 1e12, 2),
+        "pct_mfma_peak_layer": round(100 * layer_flops_6 / (ms_per_step * 1e-3) / 1e12 / peak_tf, 2),
+        "layer_gbps_algorithmic": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "kernels": per_kernel,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -52,8 +52,8 @@ E4M3_MAX = 448.0
 # --------------------------------------------------------------------------------------------
 # Codecs
 # --------------------------------------------------------------------------------------------
-def e4m3_decode(codes) -> np.ndarray:
-    """OCP FP8 E4M3 ("fn" variant) decode to float64.
+def _e4m3_value(codes) -> np.ndarray:
+    """OCP FP8 E4M3 ("fn" variant) value of each code, as float64.
 
     Bit layout s.eeee.mmm, exponent bias 7; exponent 0 holds subnormals
     m/8 * 2^-6; S.1111.111 is NaN and there is no infinity.
@@ -69,8 +69,16 @@ def e4m3_decode(codes) -> np.ndarray:
     return sign * mag
 
 
+_E4M3_TABLE = _e4m3_value(np.arange(256))
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Decode e4m3 codes (any integer array) to float64 by the table of all 256 values."""
+    return _E4M3_TABLE[np.asarray(codes, dtype=np.int64) & 0xFF]
+
+
 # The 127 non-negative finite magnitudes, ascending; their index is the code.
-_E4M3_POS = e4m3_decode(np.arange(127))
+_E4M3_POS = _E4M3_TABLE[:127]
 
 
 def e4m3_encode(x) -> np.ndarray:
@@ -184,8 +192,7 @@ def align(topk_ids, num_experts: int, block_m: int) -> Alignment:
     rows = max_padded_slots(N, E, BM)
     sorted_slots = [N] * rows
     slot_row = [-1] * N
-    cursor = offsets[:E]
-    cursor = list(cursor)
+    cursor = list(offsets[:E])
     for s in range(N):                         # ascending s keeps each expert's slots sorted
         e = int(ids[s])
         if 0 <= e < E:

@@ -1,0 +1,258 @@
+// C ABI of libmoe: host-side validation, block-size choice, workspace layout and the
+// launch sequence.  Every check runs before the first HIP call of an entry point, so
+// a rejected call enqueues nothing.
+#include <string.h>
+
+#include <mutex>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int64_t kI32Max = 2147483647LL;
+
+int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+int elt_bytes(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 2 : 1; }
+
+int32_t choose_block_m(const moe_problem* p) {
+  if (p->block_m) return p->block_m;
+  // Expected slots per expert, m = T*top_k/E.  Few slots per expert: the m-block
+  // should hold a whole expert so each weight tile is streamed from HBM once;
+  // many slots: 128-row blocks keep the MFMA tiles large.
+  const double m = (double)p->T * p->top_k / p->E;
+  if (m <= 8) return 16;
+  if (m <= 20) return 32;
+  if (m <= 40) return 64;
+  return 128;
+}
+
+int validate(const moe_problem* p) {
+  if (!p) return MOE_ERR_NULL;
+  if (p->T < 1 || p->E < 1 || p->E > 1024 || p->top_k < 1 || p->top_k > p->E) return MOE_ERR_SHAPE;
+  if (p->H < 128 || p->I < 128 || p->H % 128 || p->I % 128) return MOE_ERR_SHAPE;
+  if (p->block_m != 0 && p->block_m != 16 && p->block_m != 32 && p->block_m != 64 &&
+      p->block_m != 128)
+    return MOE_ERR_SHAPE;
+  const bool f32 = p->dtype == MOE_F32 && p->w_dtype == MOE_F32;
+  const bool bf16 = p->dtype == MOE_BF16 && p->w_dtype == MOE_BF16;
+  const bool fp8 = p->dtype == MOE_BF16 && p->w_dtype == MOE_E4M3;
+  if (!(f32 || bf16 || fp8)) return MOE_ERR_DTYPE;
+  const int64_t N = (int64_t)p->T * p->top_k;
+  const int64_t BM = choose_block_m(p);
+  const int64_t rows = N + (int64_t)(p->E < N ? p->E : N) * (BM - 1);
+  const int we = elt_bytes(p->w_dtype);
+  if (N > kI32Max || rows > kI32Max) return MOE_ERR_SHAPE;
+  if ((int64_t)2 * p->I * p->H * we > kI32Max) return MOE_ERR_SHAPE;       // one expert slab
+  if ((int64_t)p->T * p->H > kI32Max || rows * p->I > kI32Max * 4 || N * p->H > kI32Max * 4)
+    return MOE_ERR_SHAPE;
+  // grid bound of the GEMM launches
+  const int64_t tiles = rows / BM;
+  const int64_t nb = (p->I > p->H ? p->I : p->H) / 128;
+  if (tiles * nb > kI32Max) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+Resolved resolve(const moe_problem* p) {
+  Resolved r;
+  r.T = p->T; r.H = p->H; r.I = p->I; r.E = p->E; r.K = p->top_k;
+  r.BM = choose_block_m(p);
+  r.dtype = p->dtype; r.w_dtype = p->w_dtype;
+  r.N = (int64_t)p->T * p->top_k;
+  r.rows_max = r.N + (int64_t)(p->E < r.N ? p->E : r.N) * (r.BM - 1);
+  r.tiles_max = r.rows_max / r.BM;
+  return r;
+}
+
+// Workspace pieces of moe_forward, in order, each 256-byte aligned.
+struct Layout {
+  int64_t status, counts, offsets, sorted_slots, slot_row, tiles, num_tiles;
+  int64_t xq, x_scales, act, act_scales, slot_out, total;
+};
+
+Layout layout(const Resolved& r) {
+  Layout L;
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) { int64_t at = o; o = align_up(o + bytes, 256); return at; };
+  const bool fp8 = r.w_dtype == MOE_E4M3;
+  L.status = take(256);
+  L.counts = take(4LL * r.E);
+  L.offsets = take(4LL * (r.E + 1));
+  L.sorted_slots = take(4LL * r.rows_max);
+  L.slot_row = take(4LL * r.N);
+  L.tiles = take(8LL * r.tiles_max);
+  L.num_tiles = take(4);
+  L.xq = fp8 ? take((int64_t)r.T * r.H) : -1;
+  L.x_scales = fp8 ? take(4LL * r.T * (r.H / kGroup)) : -1;
+  L.act = take(r.rows_max * r.I * (fp8 ? 1 : elt_bytes(r.dtype)));
+  L.act_scales = fp8 ? take(4LL * r.rows_max * (r.I / kGroup)) : -1;
+  L.slot_out = take(r.N * r.H * elt_bytes(r.dtype));
+  L.total = o;
+  return L;
+}
+
+// gfx950 check, cached per device ordinal.
+int check_device() {
+  static std::mutex mu;
+  static int8_t ok[64];   // 0 unknown, 1 ok, -1 not gfx950
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_DEVICE;
+  std::lock_guard<std::mutex> g(mu);
+  if (ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_DEVICE;
+    ok[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+  }
+  return ok[dev] == 1 ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: dimension out of range or not a supported multiple";
+    case MOE_ERR_DTYPE: return "MOE_ERR_DTYPE: unsupported dtype combination";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH: kernel launch failed";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE: no gfx950 device current";
+    default: return "unknown moe_status";
+  }
+}
+
+int moe_validate(const moe_problem* p) { return validate(p); }
+
+int32_t moe_pick_block_m(const moe_problem* p) {
+  const int v = validate(p);
+  return v != MOE_OK ? v : choose_block_m(p);
+}
+
+int64_t moe_max_padded_slots(const moe_problem* p) {
+  const int v = validate(p);
+  return v != MOE_OK ? v : resolve(p).rows_max;
+}
+
+int64_t moe_max_tiles(const moe_problem* p) {
+  const int v = validate(p);
+  return v != MOE_OK ? v : resolve(p).tiles_max;
+}
+
+int64_t moe_workspace_bytes(const moe_problem* p) {
+  const int v = validate(p);
+  return v != MOE_OK ? v : layout(resolve(p)).total;
+}
+
+int moe_align(const moe_problem* p, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
+              int32_t* sorted_slots, int32_t* slot_row, int32_t* tiles, int32_t* num_tiles,
+              int32_t* n_invalid, void* stream) {
+  int v = validate(p);
+  if (v) return v;
+  if (!topk_ids || !counts || !offsets || !sorted_slots || !slot_row || !tiles || !num_tiles ||
+      !n_invalid)
+    return MOE_ERR_NULL;
+  if ((v = check_device())) return v;
+  const Resolved r = resolve(p);
+  return status_of(launch_align(r, topk_ids, counts, offsets, sorted_slots, slot_row, tiles,
+                                num_tiles, n_invalid, (hipStream_t)stream));
+}
+
+int moe_quantize_rows_e4m3(const moe_problem* p, const void* x, uint8_t* xq, float* scales,
+                           void* stream) {
+  int v = validate(p);
+  if (v) return v;
+  if (p->w_dtype != MOE_E4M3) return MOE_ERR_DTYPE;
+  if (!x || !xq || !scales) return MOE_ERR_NULL;
+  if ((v = check_device())) return v;
+  return status_of(launch_quant_rows(resolve(p), x, xq, scales, (hipStream_t)stream));
+}
+
+int moe_grouped_gemm_up(const moe_problem* p, const void* x, const float* x_scales,
+                        const void* w13, const float* w13_scales, const int32_t* sorted_slots,
+                        const int32_t* tiles, const int32_t* num_tiles, void* act,
+                        float* act_scales, void* stream) {
+  int v = validate(p);
+  if (v) return v;
+  if (!x || !w13 || !sorted_slots || !tiles || !num_tiles || !act) return MOE_ERR_NULL;
+  if (p->w_dtype == MOE_E4M3 && (!x_scales || !w13_scales || !act_scales)) return MOE_ERR_NULL;
+  if ((v = check_device())) return v;
+  return status_of(launch_up(resolve(p), x, x_scales, w13, w13_scales, sorted_slots, tiles,
+                             num_tiles, act, act_scales, (hipStream_t)stream));
+}
+
+int moe_grouped_gemm_down(const moe_problem* p, const void* act, const float* act_scales,
+                          const void* w2, const float* w2_scales, const float* topk_weights,
+                          const int32_t* sorted_slots, const int32_t* tiles,
+                          const int32_t* num_tiles, void* slot_out, void* stream) {
+  int v = validate(p);
+  if (v) return v;
+  if (!act || !w2 || !topk_weights || !sorted_slots || !tiles || !num_tiles || !slot_out)
+    return MOE_ERR_NULL;
+  if (p->w_dtype == MOE_E4M3 && (!act_scales || !w2_scales)) return MOE_ERR_NULL;
+  if ((v = check_device())) return v;
+  return status_of(launch_down(resolve(p), act, act_scales, w2, w2_scales, topk_weights,
+                               sorted_slots, tiles, num_tiles, slot_out, (hipStream_t)stream));
+}
+
+int moe_combine(const moe_problem* p, const void* slot_out, const int32_t* slot_row, void* out,
+                void* stream) {
+  int v = validate(p);
+  if (v) return v;
+  if (!slot_out || !slot_row || !out) return MOE_ERR_NULL;
+  if ((v = check_device())) return v;
+  return status_of(launch_combine(resolve(p), slot_out, slot_row, out, (hipStream_t)stream));
+}
+
+int moe_forward(const moe_problem* p, const void* x, const int32_t* topk_ids,
+                const float* topk_weights, const void* w13, const float* w13_scales,
+                const void* w2, const float* w2_scales, void* out, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  int v = validate(p);
+  if (v) return v;
+  if (!x || !topk_ids || !topk_weights || !w13 || !w2 || !out || !workspace) return MOE_ERR_NULL;
+  const bool fp8 = p->w_dtype == MOE_E4M3;
+  if (fp8 && (!w13_scales || !w2_scales)) return MOE_ERR_NULL;
+  const Resolved r = resolve(p);
+  const Layout L = layout(r);
+  if ((int64_t)workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if ((v = check_device())) return v;
+
+  char* ws = (char*)workspace;
+  auto at = [&](int64_t off) { return off < 0 ? nullptr : (void*)(ws + off); };
+  int32_t* n_invalid = (int32_t*)at(L.status);
+  int32_t* counts = (int32_t*)at(L.counts);
+  int32_t* offsets = (int32_t*)at(L.offsets);
+  int32_t* sorted_slots = (int32_t*)at(L.sorted_slots);
+  int32_t* slot_row = (int32_t*)at(L.slot_row);
+  int32_t* tiles = (int32_t*)at(L.tiles);
+  int32_t* num_tiles = (int32_t*)at(L.num_tiles);
+  hipStream_t s = (hipStream_t)stream;
+
+  hipError_t e = launch_align(r, topk_ids, counts, offsets, sorted_slots, slot_row, tiles,
+                              num_tiles, n_invalid, s);
+  if (e != hipSuccess) return MOE_ERR_LAUNCH;
+  const void* x_in = x;
+  const float* x_scales = nullptr;
+  if (fp8) {
+    e = launch_quant_rows(r, x, (uint8_t*)at(L.xq), (float*)at(L.x_scales), s);
+    if (e != hipSuccess) return MOE_ERR_LAUNCH;
+    x_in = at(L.xq);
+    x_scales = (const float*)at(L.x_scales);
+  }
+  e = launch_up(r, x_in, x_scales, w13, w13_scales, sorted_slots, tiles, num_tiles, at(L.act),
+                (float*)at(L.act_scales), s);
+  if (e != hipSuccess) return MOE_ERR_LAUNCH;
+  e = launch_down(r, at(L.act), (const float*)at(L.act_scales), w2, w2_scales, topk_weights,
+                  sorted_slots, tiles, num_tiles, at(L.slot_out), s);
+  if (e != hipSuccess) return MOE_ERR_LAUNCH;
+  e = launch_combine(r, at(L.slot_out), slot_row, out, s);
+  return status_of(e);
+}
+
+}  // extern "C"

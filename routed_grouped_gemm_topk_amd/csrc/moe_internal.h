@@ -1,0 +1,97 @@
+// Internal declarations shared by the HIP translation units of libmoe (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------------------------
+// Vector types for the gfx950 MFMA builtins
+// ---------------------------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr int kGroup = 128;      // fp8 weight block edge and activation group width
+constexpr float kE4M3Max = 448.0f;
+
+// ---------------------------------------------------------------------------------------------
+// Scalar conversions
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// Round-to-nearest-even float -> bfloat16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// OCP E4M3 ("fn") encode: round to nearest even, saturate to +-448, sign kept.
+// Written from the format: 4 exponent bits (bias 7), 3 mantissa bits, subnormal
+// step 2^-9, largest finite 1.75 * 2^8.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = fminf(fabsf(f), kE4M3Max);
+  uint32_t code;
+  if (a < 0.015625f) {                       // below 2^-6: subnormal grid of step 2^-9
+    // a * 2^9 is exact; rint rounds half to even
+    code = (uint32_t)__builtin_rintf(a * 512.0f);   // 0..8 (8 = smallest normal 2^-6)
+  } else {
+    uint32_t ua = __float_as_uint(a);
+    // keep 3 mantissa bits with round-half-even on the 20 discarded bits
+    uint32_t lsb = (ua >> 20) & 1u;
+    ua += 0x7FFFFu + lsb;
+    uint32_t e = (ua >> 23) - 127 + 7;       // rebias; rounding may have bumped the exponent
+    uint32_t m = (ua >> 20) & 7u;
+    code = (e << 3) | m;
+    if (code > 0x7Eu) code = 0x7Eu;          // a <= 448 already; guards the bump past 448
+  }
+  return sign | code;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Launchers (host side), one per translation unit
+// ---------------------------------------------------------------------------------------------
+struct Resolved {
+  int32_t T, H, I, E, K;   // K = top_k
+  int32_t BM;
+  int32_t dtype, w_dtype;
+  int64_t N;               // T*top_k
+  int64_t rows_max;        // moe_max_padded_slots
+  int64_t tiles_max;       // moe_max_tiles
+};
+
+hipError_t launch_align(const Resolved& r, const int32_t* ids, int32_t* counts, int32_t* offsets,
+                        int32_t* sorted_slots, int32_t* slot_row, int32_t* tiles,
+                        int32_t* num_tiles, int32_t* n_invalid, hipStream_t s);
+
+hipError_t launch_quant_rows(const Resolved& r, const void* x, uint8_t* xq, float* scales,
+                             hipStream_t s);
+
+hipError_t launch_up(const Resolved& r, const void* x, const float* x_scales, const void* w13,
+                     const float* w13_scales, const int32_t* sorted_slots, const int32_t* tiles,
+                     const int32_t* num_tiles, void* act, float* act_scales, hipStream_t s);
+
+hipError_t launch_down(const Resolved& r, const void* act, const float* act_scales,
+                       const void* w2, const float* w2_scales, const float* topk_w,
+                       const int32_t* sorted_slots, const int32_t* tiles,
+                       const int32_t* num_tiles, void* slot_out, hipStream_t s);
+
+hipError_t launch_combine(const Resolved& r, const void* slot_out, const int32_t* slot_row,
+                          void* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,115 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function that
+include/moe.h declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import routed_grouped_gemm_topk_amd as moe
+from routed_grouped_gemm_topk_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moe.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return moe.load()
+
+
+def test_header_declares_the_binding_exports():
+    assert header_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(-6, 1):
+        assert moe.status_str(code).startswith("MOE_")
+    assert "unknown" in moe.status_str(-99)
+
+
+def bad(**kw):
+    base = dict(T=16, H=128, I=256, E=8, top_k=2, dtype="bf16")
+    base.update(kw)
+    return moe.make_problem(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0), moe.MOE_ERR_SHAPE), (dict(H=100), moe.MOE_ERR_SHAPE), (dict(I=192), moe.MOE_ERR_SHAPE),
+    (dict(E=0), moe.MOE_ERR_SHAPE), (dict(E=1025, top_k=2), moe.MOE_ERR_SHAPE),
+    (dict(top_k=0), moe.MOE_ERR_SHAPE), (dict(top_k=9), moe.MOE_ERR_SHAPE),
+    (dict(block_m=48), moe.MOE_ERR_SHAPE), (dict(block_m=256), moe.MOE_ERR_SHAPE),
+    (dict(dtype="f32", w_dtype="bf16"), moe.MOE_ERR_DTYPE), (dict(dtype="e4m3"), moe.MOE_ERR_DTYPE),
+    (dict(dtype="f32", w_dtype="e4m3"), moe.MOE_ERR_DTYPE),
+    (dict(H=2 ** 16, I=2 ** 15), moe.MOE_ERR_SHAPE),            # one expert slab >= 2^31 bytes
+])
+def test_validation_codes(kw, code):
+    assert moe.moe_validate(bad(**kw)) == code
+    with pytest.raises(moe.MoeError):
+        moe.moe_workspace_bytes(bad(**kw))
+
+
+def test_null_problem(lib):
+    assert lib.moe_validate(None) == moe.MOE_ERR_NULL
+    assert lib.moe_align(None, *([None] * 9)) == moe.MOE_ERR_NULL
+
+
+def test_entry_points_reject_before_any_hip_call(lib):
+    """Shape errors win over NULL pointers, NULL pointers over device checks, and a short
+    workspace is reported before the device is touched (this host has no GPU)."""
+    p = bad(H=100)
+    P = ctypes.byref(p)
+    assert lib.moe_align(P, *([None] * 9)) == moe.MOE_ERR_SHAPE
+    assert lib.moe_grouped_gemm_up(P, *([None] * 10)) == moe.MOE_ERR_SHAPE
+    assert lib.moe_grouped_gemm_down(P, *([None] * 10)) == moe.MOE_ERR_SHAPE
+    assert lib.moe_combine(P, None, None, None, None) == moe.MOE_ERR_SHAPE
+    assert lib.moe_forward(P, *([None] * 9), 0, None) == moe.MOE_ERR_SHAPE
+    p = bad()
+    P = ctypes.byref(p)
+    assert lib.moe_align(P, *([None] * 9)) == moe.MOE_ERR_NULL
+    assert lib.moe_grouped_gemm_up(P, *([None] * 10)) == moe.MOE_ERR_NULL
+    assert lib.moe_grouped_gemm_down(P, *([None] * 10)) == moe.MOE_ERR_NULL
+    assert lib.moe_combine(P, None, None, None, None) == moe.MOE_ERR_NULL
+    assert lib.moe_quantize_rows_e4m3(P, 8, 8, 8, None) == moe.MOE_ERR_DTYPE   # bf16 weights
+    fake = [ctypes.c_void_p(256)] * 9
+    need = moe.moe_workspace_bytes(p)
+    assert lib.moe_forward(P, *fake, need - 1, None) == moe.MOE_ERR_WORKSPACE
+    pf = bad(w_dtype="e4m3")
+    assert lib.moe_forward(ctypes.byref(pf), *fake[:4], None, fake[5], None, fake[7], fake[8],
+                           10 ** 12, None) == moe.MOE_ERR_NULL
+
+
+@pytest.mark.parametrize("T,H,I,E,k,dt,wdt,bm", [
+    (16, 128, 256, 8, 2, "f32", "f32", 16), (4096, 4096, 14336, 8, 2, "bf16", "bf16", 128),
+    (64, 7168, 2048, 256, 8, "bf16", "bf16", 16), (8192, 2048, 1408, 64, 6, "bf16", "bf16", 128),
+    (2048, 7168, 2048, 256, 8, "bf16", "e4m3", 128), (1, 128, 128, 4, 1, "bf16", "bf16", 16),
+])
+def test_block_m_choice_and_bounds(T, H, I, E, k, dt, wdt, bm):
+    p = moe.make_problem(T, H, I, E, k, dt, wdt)
+    assert moe.moe_pick_block_m(p) == bm
+    assert moe.moe_max_padded_slots(p) == oracle.max_padded_slots(T * k, E, bm)
+    assert moe.moe_max_tiles(p) == oracle.max_tiles(T * k, E, bm)
+    for forced in (16, 32, 64, 128):
+        q = moe.make_problem(T, H, I, E, k, dt, wdt, block_m=forced)
+        assert moe.moe_pick_block_m(q) == forced
+        assert moe.moe_max_tiles(q) == oracle.max_tiles(T * k, E, forced)
+    assert moe.moe_workspace_bytes(p) % 256 == 0
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    p = bad()
+    with pytest.raises(ValueError):
+        moe.moe_combine(p, torch.zeros(16 * 2 * 128, dtype=torch.bfloat16),
+                        torch.zeros(32, dtype=torch.int32), torch.zeros(16 * 128, dtype=torch.bfloat16))
