@@ -33,6 +33,7 @@ int validate(const moe_problem* p) {
   if (!p) return MOE_ERR_NULL;
   if (p->T < 1 || p->E < 1 || p->E > 1024 || p->top_k < 1 || p->top_k > p->E) return MOE_ERR_SHAPE;
   if (p->H < 128 || p->I < 128 || p->H % 128 || p->I % 128) return MOE_ERR_SHAPE;
+  if (p->H > kMaxDim || p->I > kMaxDim) return MOE_ERR_SHAPE;
   if (p->block_m != 0 && p->block_m != 16 && p->block_m != 32 && p->block_m != 64 &&
       p->block_m != 128)
     return MOE_ERR_SHAPE;

@@ -419,6 +419,8 @@ static hipError_t dispatch_bm(const Resolved& r, const GemmArgs& a, hipStream_t 
 hipError_t launch_up(const Resolved& r, const void* x, const float* x_scales, const void* w13,
                      const float* w13_scales, const int32_t* sorted_slots, const int32_t* tiles,
                      const int32_t* num_tiles, void* act, float* act_scales, hipStream_t s) {
+  if (prefill_supported(r))
+    return launch_up_prefill(r, x, w13, sorted_slots, tiles, num_tiles, act, s);
   GemmArgs a{};
   a.a_src = (const char*)x;
   a.a_scales = x_scales;
@@ -445,6 +447,8 @@ hipError_t launch_down(const Resolved& r, const void* act, const float* act_scal
                        const void* w2, const float* w2_scales, const float* topk_w,
                        const int32_t* sorted_slots, const int32_t* tiles,
                        const int32_t* num_tiles, void* slot_out, hipStream_t s) {
+  if (prefill_supported(r))
+    return launch_down_prefill(r, act, w2, topk_w, sorted_slots, tiles, num_tiles, slot_out, s);
   GemmArgs a{};
   a.a_src = (const char*)act;
   a.a_scales = act_scales;

@@ -19,6 +19,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 constexpr int kGroup = 128;      // fp8 weight block edge and activation group width
+constexpr int kMaxDim = 32768;   // largest supported H and I
 constexpr float kE4M3Max = 448.0f;
 
 // ---------------------------------------------------------------------------------------------
@@ -90,6 +91,16 @@ hipError_t launch_down(const Resolved& r, const void* act, const float* act_scal
                        const void* w2, const float* w2_scales, const float* topk_w,
                        const int32_t* sorted_slots, const int32_t* tiles,
                        const int32_t* num_tiles, void* slot_out, hipStream_t s);
+
+// bf16 kernels for 128-row m-blocks (MFMA 32x32x16), used by launch_up / launch_down.
+bool prefill_supported(const Resolved& r);
+hipError_t launch_up_prefill(const Resolved& r, const void* x, const void* w13,
+                             const int32_t* sorted_slots, const int32_t* tiles,
+                             const int32_t* num_tiles, void* act, hipStream_t s);
+hipError_t launch_down_prefill(const Resolved& r, const void* act, const void* w2,
+                               const float* topk_w, const int32_t* sorted_slots,
+                               const int32_t* tiles, const int32_t* num_tiles, void* slot_out,
+                               hipStream_t s);
 
 hipError_t launch_combine(const Resolved& r, const void* slot_out, const int32_t* slot_row,
                           void* out, hipStream_t s);

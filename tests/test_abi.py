@@ -52,7 +52,8 @@ def bad(**kw):
     (dict(block_m=48), moe.MOE_ERR_SHAPE), (dict(block_m=256), moe.MOE_ERR_SHAPE),
     (dict(dtype="f32", w_dtype="bf16"), moe.MOE_ERR_DTYPE), (dict(dtype="e4m3"), moe.MOE_ERR_DTYPE),
     (dict(dtype="f32", w_dtype="e4m3"), moe.MOE_ERR_DTYPE),
-    (dict(H=2 ** 16, I=2 ** 15), moe.MOE_ERR_SHAPE),            # one expert slab >= 2^31 bytes
+    (dict(H=2 ** 15 + 128), moe.MOE_ERR_SHAPE),                  # above the largest H
+    (dict(H=2 ** 15, I=2 ** 15, dtype="f32"), moe.MOE_ERR_SHAPE),  # one expert slab >= 2^31 bytes
 ])
 def test_validation_codes(kw, code):
     assert moe.moe_validate(bad(**kw)) == code
