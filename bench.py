@@ -190,11 +190,11 @@ def main():
             moe.moe_quantize_rows_e4m3(p, case.x, xq, x_scales)
             x_in = xq
             mark()
-        moe.moe_grouped_gemm_up(p, x_in, x_scales, case.w13, case.w13_scales, a["sorted_slots"],
+        moe.moe_grouped_gemm_up(p, x_in, x_scales, case.w13, case.w13_scales, a["sorted_slots"], a["offsets"],
                                 a["tiles"], a["num_tiles"], act, act_scales)
         mark()
         moe.moe_grouped_gemm_down(p, act, act_scales, case.w2, case.w2_scales, case.topk_weights,
-                                  a["sorted_slots"], a["tiles"], a["num_tiles"], slot_out)
+                                  a["sorted_slots"], a["offsets"], a["tiles"], a["num_tiles"], slot_out)
         mark()
         moe.moe_combine(p, slot_out, a["slot_row"], out)
         mark()

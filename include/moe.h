@@ -148,7 +148,7 @@ int moe_quantize_rows_e4m3(const moe_problem* p, const void* x, uint8_t* xq, flo
  * In:  x        dtype [T,H]; for E4M3 weights: the e4m3 codes [T,H] from
  *               moe_quantize_rows_e4m3 with x_scales fp32 [T,H/128] (else x_scales NULL)
  *      w13      w_dtype [E, 2I, H]; w13_scales fp32 [E, 2I/128, H/128] for E4M3 (else NULL)
- *      sorted_slots, tiles, num_tiles: outputs of moe_align for the same problem
+ *      sorted_slots, offsets, tiles, num_tiles: outputs of moe_align for the same problem
  * Out: act      [moe_max_padded_slots, I]: dtype, or e4m3 codes for E4M3 weights with
  *               act_scales fp32 [moe_max_padded_slots, I/128] (amax/448 per row and
  *               128-column group, as above).  Rows of valid tiles are written (padding
@@ -156,8 +156,8 @@ int moe_quantize_rows_e4m3(const moe_problem* p, const void* x, uint8_t* xq, flo
  */
 int moe_grouped_gemm_up(const moe_problem* p, const void* x, const float* x_scales,
                         const void* w13, const float* w13_scales, const int32_t* sorted_slots,
-                        const int32_t* tiles, const int32_t* num_tiles, void* act,
-                        float* act_scales, void* stream);
+                        const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles,
+                        void* act, float* act_scales, void* stream);
 
 /*
  * moe_grouped_gemm_down -- down projection with the routing weight in the epilogue.
@@ -168,13 +168,15 @@ int moe_grouped_gemm_up(const moe_problem* p, const void* x, const float* x_scal
  * In:  act, act_scales  as written by moe_grouped_gemm_up
  *      w2  w_dtype [E, H, I]; w2_scales fp32 [E, H/128, I/128] for E4M3 (else NULL)
  *      topk_weights fp32 [T, top_k]
+ *      sorted_slots, offsets, tiles, num_tiles: outputs of moe_align for the same problem
  * Out: slot_out dtype [N, H] (bf16 for E4M3 weights).  Rows of excluded slots
  *      are not written.
  */
 int moe_grouped_gemm_down(const moe_problem* p, const void* act, const float* act_scales,
                           const void* w2, const float* w2_scales, const float* topk_weights,
-                          const int32_t* sorted_slots, const int32_t* tiles,
-                          const int32_t* num_tiles, void* slot_out, void* stream);
+                          const int32_t* sorted_slots, const int32_t* offsets,
+                          const int32_t* tiles, const int32_t* num_tiles, void* slot_out,
+                          void* stream);
 
 /*
  * moe_combine -- deterministic per-token combine, no atomics.

@@ -82,8 +82,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "moe_workspace_bytes": (ctypes.c_int64, [P]),
         "moe_align": (ctypes.c_int, [P] + [vp] * 8 + [vp]),
         "moe_quantize_rows_e4m3": (ctypes.c_int, [P, vp, vp, vp, vp]),
-        "moe_grouped_gemm_up": (ctypes.c_int, [P] + [vp] * 9 + [vp]),
-        "moe_grouped_gemm_down": (ctypes.c_int, [P] + [vp] * 9 + [vp]),
+        "moe_grouped_gemm_up": (ctypes.c_int, [P] + [vp] * 10 + [vp]),
+        "moe_grouped_gemm_down": (ctypes.c_int, [P] + [vp] * 10 + [vp]),
         "moe_combine": (ctypes.c_int, [P, vp, vp, vp, vp]),
         "moe_forward": (ctypes.c_int, [P] + [vp] * 9 + [ctypes.c_size_t, vp]),
     }
@@ -190,8 +190,8 @@ def moe_quantize_rows_e4m3(p: Problem, x, xq, scales, stream=None) -> None:
              "moe_quantize_rows_e4m3")
 
 
-def moe_grouped_gemm_up(p: Problem, x, x_scales, w13, w13_scales, sorted_slots, tiles, num_tiles,
-                        act, act_scales, stream=None) -> None:
+def moe_grouped_gemm_up(p: Problem, x, x_scales, w13, w13_scales, sorted_slots, offsets, tiles,
+                        num_tiles, act, act_scales, stream=None) -> None:
     rows = moe_max_padded_slots(p)
     fp8 = p.w_dtype == MOE_E4M3
     xdt = (torch.uint8, torch.float8_e4m3fn) if fp8 else _TORCH_DT[p.dtype]
@@ -200,6 +200,7 @@ def moe_grouped_gemm_up(p: Problem, x, x_scales, w13, w13_scales, sorted_slots, 
             _ptr(w13, "w13", _w_dtype(p), p.E * 2 * p.I * p.H),
             _ptr(w13_scales, "w13_scales", torch.float32, p.E * (2 * p.I // 128) * (p.H // 128)),
             _ptr(sorted_slots, "sorted_slots", torch.int32, rows),
+            _ptr(offsets, "offsets", torch.int32, p.E + 1),
             _ptr(tiles, "tiles", torch.int32, 2 * moe_max_tiles(p)),
             _ptr(num_tiles, "num_tiles", torch.int32, 1),
             _ptr(act, "act", (_act_dtype(p), torch.float8_e4m3fn) if fp8 else _act_dtype(p), rows * p.I),
@@ -209,7 +210,7 @@ def moe_grouped_gemm_up(p: Problem, x, x_scales, w13, w13_scales, sorted_slots, 
 
 
 def moe_grouped_gemm_down(p: Problem, act, act_scales, w2, w2_scales, topk_weights, sorted_slots,
-                          tiles, num_tiles, slot_out, stream=None) -> None:
+                          offsets, tiles, num_tiles, slot_out, stream=None) -> None:
     rows = moe_max_padded_slots(p)
     fp8 = p.w_dtype == MOE_E4M3
     args = [_ptr(act, "act", (_act_dtype(p), torch.float8_e4m3fn) if fp8 else _act_dtype(p), rows * p.I),
@@ -218,6 +219,7 @@ def moe_grouped_gemm_down(p: Problem, act, act_scales, w2, w2_scales, topk_weigh
             _ptr(w2_scales, "w2_scales", torch.float32, p.E * (p.H // 128) * (p.I // 128)),
             _ptr(topk_weights, "topk_weights", torch.float32, p.T * p.top_k),
             _ptr(sorted_slots, "sorted_slots", torch.int32, rows),
+            _ptr(offsets, "offsets", torch.int32, p.E + 1),
             _ptr(tiles, "tiles", torch.int32, 2 * moe_max_tiles(p)),
             _ptr(num_tiles, "num_tiles", torch.int32, 1),
             _ptr(slot_out, "slot_out", _TORCH_DT[p.dtype], p.T * p.top_k * p.H)]

@@ -176,29 +176,32 @@ int moe_quantize_rows_e4m3(const moe_problem* p, const void* x, uint8_t* xq, flo
 
 int moe_grouped_gemm_up(const moe_problem* p, const void* x, const float* x_scales,
                         const void* w13, const float* w13_scales, const int32_t* sorted_slots,
-                        const int32_t* tiles, const int32_t* num_tiles, void* act,
-                        float* act_scales, void* stream) {
+                        const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles,
+                        void* act, float* act_scales, void* stream) {
   int v = validate(p);
   if (v) return v;
-  if (!x || !w13 || !sorted_slots || !tiles || !num_tiles || !act) return MOE_ERR_NULL;
+  if (!x || !w13 || !sorted_slots || !offsets || !tiles || !num_tiles || !act) return MOE_ERR_NULL;
   if (p->w_dtype == MOE_E4M3 && (!x_scales || !w13_scales || !act_scales)) return MOE_ERR_NULL;
   if ((v = check_device())) return v;
-  return status_of(launch_up(resolve(p), x, x_scales, w13, w13_scales, sorted_slots, tiles,
-                             num_tiles, act, act_scales, (hipStream_t)stream));
+  return status_of(launch_up(resolve(p), x, x_scales, w13, w13_scales, sorted_slots, offsets,
+                             tiles, num_tiles, act, act_scales, (hipStream_t)stream));
 }
 
 int moe_grouped_gemm_down(const moe_problem* p, const void* act, const float* act_scales,
                           const void* w2, const float* w2_scales, const float* topk_weights,
-                          const int32_t* sorted_slots, const int32_t* tiles,
-                          const int32_t* num_tiles, void* slot_out, void* stream) {
+                          const int32_t* sorted_slots, const int32_t* offsets,
+                          const int32_t* tiles, const int32_t* num_tiles, void* slot_out,
+                          void* stream) {
   int v = validate(p);
   if (v) return v;
-  if (!act || !w2 || !topk_weights || !sorted_slots || !tiles || !num_tiles || !slot_out)
+  if (!act || !w2 || !topk_weights || !sorted_slots || !offsets || !tiles || !num_tiles ||
+      !slot_out)
     return MOE_ERR_NULL;
   if (p->w_dtype == MOE_E4M3 && (!act_scales || !w2_scales)) return MOE_ERR_NULL;
   if ((v = check_device())) return v;
   return status_of(launch_down(resolve(p), act, act_scales, w2, w2_scales, topk_weights,
-                               sorted_slots, tiles, num_tiles, slot_out, (hipStream_t)stream));
+                               sorted_slots, offsets, tiles, num_tiles, slot_out,
+                               (hipStream_t)stream));
 }
 
 int moe_combine(const moe_problem* p, const void* slot_out, const int32_t* slot_row, void* out,
@@ -246,11 +249,11 @@ int moe_forward(const moe_problem* p, const void* x, const int32_t* topk_ids,
     x_in = at(L.xq);
     x_scales = (const float*)at(L.x_scales);
   }
-  e = launch_up(r, x_in, x_scales, w13, w13_scales, sorted_slots, tiles, num_tiles, at(L.act),
-                (float*)at(L.act_scales), s);
+  e = launch_up(r, x_in, x_scales, w13, w13_scales, sorted_slots, offsets, tiles, num_tiles,
+                at(L.act), (float*)at(L.act_scales), s);
   if (e != hipSuccess) return MOE_ERR_LAUNCH;
   e = launch_down(r, at(L.act), (const float*)at(L.act_scales), w2, w2_scales, topk_weights,
-                  sorted_slots, tiles, num_tiles, at(L.slot_out), s);
+                  sorted_slots, offsets, tiles, num_tiles, at(L.slot_out), s);
   if (e != hipSuccess) return MOE_ERR_LAUNCH;
   e = launch_combine(r, at(L.slot_out), slot_row, out, s);
   return status_of(e);

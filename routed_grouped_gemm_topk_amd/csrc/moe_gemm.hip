@@ -25,8 +25,8 @@
 //   * the grid is sized by the host-side tile bound; workgroups past the device-side
 //     tile count exit at once (no host synchronisation);
 //   * workgroup ids are remapped so each of the 8 XCDs (own L2) runs a contiguous
-//     range of tiles, and consecutive tiles share one weight tile (m-blocks of one
-//     expert at the same n-block).
+//     range of the valid tiles, and consecutive tiles share one weight tile (m-blocks
+//     at the same n-block).
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -102,9 +102,15 @@ struct GemmArgs {
   int64_t w_expert_elems;     // elements per expert weight slab
 };
 
-__device__ __forceinline__ int xcd_remap(int b, int grid) {
-  const int per = grid >> 3, rem = grid & 7, x = b & 7, i = b >> 3;
-  return (x < rem) ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
+// Work split over the 8 XCDs: block b runs on XCD b % 8; each XCD takes a contiguous range
+// of the `valid` logical tiles (device-side tile count x n-blocks), so no XCD idles on the
+// slack between the host-side tile bound and the real count.  -1: nothing to do.
+__device__ __forceinline__ int xcd_logical(int b, int valid) {
+  const int per = (valid + 7) >> 3;
+  const int i = b >> 3;
+  if (i >= per) return -1;
+  const int l = (b & 7) * per + i;
+  return l < valid ? l : -1;
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -140,10 +146,12 @@ __global__ __launch_bounds__(WM* WN* kWave) void moe_gemm_kernel(GemmArgs g) {
   const int wave = tid / kWave;
   const int wm = wave / WN, wn = wave % WN;
 
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int mt = bid % g.tiles_max;
-  const int nt = bid / g.tiles_max;
-  if (mt >= *g.num_tiles) return;
+  // logical order: m-block fastest, so consecutive workgroups share one weight tile
+  const int ntiles = *g.num_tiles;
+  const int bid = xcd_logical(blockIdx.x, ntiles * (g.n_out / BN));
+  if (bid < 0) return;
+  const int mt = bid % ntiles;
+  const int nt = bid / ntiles;
   const int e = g.tiles[2 * mt];
   const int row0 = g.tiles[2 * mt + 1];
   const int n0 = nt * BN;
@@ -395,7 +403,8 @@ __global__ __launch_bounds__(WM* WN* kWave) void moe_gemm_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------------------------
 template <class Op, int BM, int BN, int BK, int WM, int WN, bool UP, int OUT>
 static hipError_t run(const GemmArgs& a, int n_blocks_n, hipStream_t s) {
-  const int64_t grid = (int64_t)a.tiles_max * n_blocks_n;
+  // multiple of 8: every XCD's share of the valid tiles must have blocks to run on
+  const int64_t grid = ((int64_t)a.tiles_max * n_blocks_n + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL((moe_gemm_kernel<Op, BM, BN, BK, WM, WN, UP, OUT>), dim3((unsigned)grid),
                      dim3(WM * WN * kWave), 0, s, a);
@@ -417,10 +426,11 @@ static hipError_t dispatch_bm(const Resolved& r, const GemmArgs& a, hipStream_t 
 }
 
 hipError_t launch_up(const Resolved& r, const void* x, const float* x_scales, const void* w13,
-                     const float* w13_scales, const int32_t* sorted_slots, const int32_t* tiles,
-                     const int32_t* num_tiles, void* act, float* act_scales, hipStream_t s) {
+                     const float* w13_scales, const int32_t* sorted_slots, const int32_t* offsets,
+                     const int32_t* tiles, const int32_t* num_tiles, void* act, float* act_scales,
+                     hipStream_t s) {
   if (prefill_supported(r))
-    return launch_up_prefill(r, x, w13, sorted_slots, tiles, num_tiles, act, s);
+    return launch_up_prefill(r, x, w13, sorted_slots, offsets, tiles, num_tiles, act, s);
   GemmArgs a{};
   a.a_src = (const char*)x;
   a.a_scales = x_scales;
@@ -445,10 +455,11 @@ hipError_t launch_up(const Resolved& r, const void* x, const float* x_scales, co
 
 hipError_t launch_down(const Resolved& r, const void* act, const float* act_scales,
                        const void* w2, const float* w2_scales, const float* topk_w,
-                       const int32_t* sorted_slots, const int32_t* tiles,
+                       const int32_t* sorted_slots, const int32_t* offsets, const int32_t* tiles,
                        const int32_t* num_tiles, void* slot_out, hipStream_t s) {
   if (prefill_supported(r))
-    return launch_down_prefill(r, act, w2, topk_w, sorted_slots, tiles, num_tiles, slot_out, s);
+    return launch_down_prefill(r, act, w2, topk_w, sorted_slots, offsets, tiles, num_tiles,
+                               slot_out, s);
   GemmArgs a{};
   a.a_src = (const char*)act;
   a.a_scales = act_scales;

@@ -23,8 +23,9 @@
 //     requested before slice kt is multiplied, slice kt+1 (requested one slice earlier)
 //     is written to the free LDS stage after the multiply;
 //   * fragment reads of the next 16-wide k step overlap the MFMAs of the current one;
-//   * tile order: groups of 8 m-blocks sweep the n-blocks, and each XCD (own L2) runs a
-//     contiguous range of that order, so concurrent workgroups share rows and weights.
+//   * tile order: expert by expert, groups of 8 m-blocks of one expert sweep the n-blocks,
+//     and each XCD (own L2) runs a contiguous range of that order, so concurrent workgroups
+//     share rows and weights and each weight tile leaves HBM about once.
 #include "moe_internal.h"
 
 namespace moe {
@@ -45,25 +46,45 @@ __device__ __forceinline__ int swz(int r) {
   else return ((r >> 1) ^ (r >> 3)) & 3;
 }
 
-__device__ __forceinline__ int xcd_remap(int b, int grid) {
-  const int per = grid >> 3, rem = grid & 7, x = b & 7, i = b >> 3;
-  return (x < rem) ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
+// Work split over the 8 XCDs (each with its own L2): workgroups are dispatched round-robin,
+// so block b runs on XCD b % 8.  Each XCD takes one contiguous range of the `valid` logical
+// tiles (valid = device-side tile count x n-blocks); blocks past their XCD's share exit.
+// Returns -1 for such blocks.
+__device__ __forceinline__ int xcd_logical(int b, int valid) {
+  const int per = (valid + 7) >> 3;
+  const int i = b >> 3;
+  if (i >= per) return -1;
+  const int l = (b & 7) * per + i;
+  return l < valid ? l : -1;
 }
 
-// Logical tile order: groups of GROUP_M consecutive m-blocks (expert-major, so mostly
-// one expert) sweep all n-blocks, n-block-major inside the group.  The grid is
-// round_up(tiles_max, GROUP_M) * n_blocks.
-__device__ __forceinline__ void tile_of(int logical, int n_blocks, int& mt, int& nt) {
-  const int per_group = GROUP_M * n_blocks;
-  const int q = logical / per_group, w = logical - q * per_group;
-  nt = w / GROUP_M;
-  mt = q * GROUP_M + (w - nt * GROUP_M);
+// Logical tile order, expert by expert: inside expert e (m-blocks base..base+M-1) groups of
+// GROUP_M m-blocks sweep the n-blocks, n-block-major inside a group.  A group never holds two
+// experts, so one XCD's concurrent workgroups share their weight tiles (each fetched once) and
+// their gathered rows.  logical / n_blocks is an m-block of the expert that owns `logical`.
+__device__ __forceinline__ void tile_of(int logical, int n_blocks, const int32_t* tiles,
+                                        const int32_t* offsets, int& mt, int& nt) {
+  const int e = tiles[2 * (logical / n_blocks)];
+  const int base = offsets[e] / BM;
+  const int M = (offsets[e + 1] - offsets[e]) / BM;
+  const int r = logical - base * n_blocks;          // 0 <= r < M * n_blocks
+  const int full = M / GROUP_M;
+  if (r < full * GROUP_M * n_blocks) {
+    const int g = r / (GROUP_M * n_blocks), w = r - g * GROUP_M * n_blocks;
+    nt = w / GROUP_M;
+    mt = base + g * GROUP_M + (w - nt * GROUP_M);
+  } else {
+    const int rem = M - full * GROUP_M, w = r - full * GROUP_M * n_blocks;
+    nt = w / rem;
+    mt = base + full * GROUP_M + (w - nt * rem);
+  }
 }
 
 struct Args {
   const char* a_src;        // up: X [T, K]; down: act [rows_max, K]   (bf16)
   const char* w;            // up: W13 [E, 2I, K]; down: W2 [E, H, K]  (bf16)
   const int32_t* sorted_slots;
+  const int32_t* offsets;
   const int32_t* tiles;
   const int32_t* num_tiles;
   const float* topk_w;      // down
@@ -97,9 +118,11 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_kernel(Args g) {
   const int wave = tid / kWave;
   const int wm = wave / WN, wn = wave % WN;
 
+  const int nblk = g.n_out / BNA;
+  const int logical = xcd_logical(blockIdx.x, *g.num_tiles * nblk);
+  if (logical < 0) return;
   int mt, nt;
-  tile_of(xcd_remap(blockIdx.x, gridDim.x), g.n_out / BNA, mt, nt);
-  if (mt >= *g.num_tiles) return;                // also covers mt >= tiles_max
+  tile_of(logical, nblk, g.tiles, g.offsets, mt, nt);
   const int e = g.tiles[2 * mt];
   const int row0 = g.tiles[2 * mt + 1];
   const int n0 = nt * BNA;
@@ -326,9 +349,11 @@ __global__ __launch_bounds__(4 * kWave) void gemm_dma_kernel(Args g) {
   const int wave = tid / kWave;
   const int wn = wave;
 
+  const int nblk = g.n_out / BNA;
+  const int logical = xcd_logical(blockIdx.x, *g.num_tiles * nblk);
+  if (logical < 0) return;
   int mt, nt;
-  tile_of(xcd_remap(blockIdx.x, gridDim.x), g.n_out / BNA, mt, nt);
-  if (mt >= *g.num_tiles) return;
+  tile_of(logical, nblk, g.tiles, g.offsets, mt, nt);
   const int e = g.tiles[2 * mt];
   const int row0 = g.tiles[2 * mt + 1];
   const int n0 = nt * BNA;
@@ -483,8 +508,8 @@ __global__ __launch_bounds__(4 * kWave) void gemm_dma_kernel(Args g) {
 
 template <int BK, int NS, int BNA, bool UP>
 hipError_t run_dma(const Args& a, hipStream_t s) {
-  const int64_t groups = (a.tiles_max + GROUP_M - 1) / GROUP_M;
-  const int64_t grid = groups * GROUP_M * (a.n_out / BNA);
+  // multiple of 8: every XCD's share of the valid tiles must have blocks to run on
+  const int64_t grid = ((int64_t)a.tiles_max * (a.n_out / BNA) + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL((gemm_dma_kernel<BK, NS, BNA, UP>), dim3((unsigned)grid), dim3(4 * kWave), 0, s, a);
   return hipGetLastError();
@@ -492,8 +517,8 @@ hipError_t run_dma(const Args& a, hipStream_t s) {
 
 template <int BK, int WM, int WN, int BNA, bool UP>
 hipError_t run(const Args& a, hipStream_t s) {
-  const int64_t groups = (a.tiles_max + GROUP_M - 1) / GROUP_M;
-  const int64_t grid = groups * GROUP_M * (a.n_out / BNA);
+  // multiple of 8: every XCD's share of the valid tiles must have blocks to run on
+  const int64_t grid = ((int64_t)a.tiles_max * (a.n_out / BNA) + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL((gemm_kernel<BK, WM, WN, BNA, UP>), dim3((unsigned)grid), dim3(WM * WN * kWave),
                      0, s, a);
@@ -507,9 +532,11 @@ bool prefill_supported(const Resolved& r) {
 }
 
 hipError_t launch_up_prefill(const Resolved& r, const void* x, const void* w13,
-                             const int32_t* sorted_slots, const int32_t* tiles,
-                             const int32_t* num_tiles, void* act, hipStream_t s) {
+                             const int32_t* sorted_slots, const int32_t* offsets,
+                             const int32_t* tiles, const int32_t* num_tiles, void* act,
+                             hipStream_t s) {
   pf::Args a{};
+  a.offsets = offsets;
   a.a_src = (const char*)x;
   a.w = (const char*)w13;
   a.sorted_slots = sorted_slots;
@@ -528,9 +555,10 @@ hipError_t launch_up_prefill(const Resolved& r, const void* x, const void* w13,
 
 hipError_t launch_down_prefill(const Resolved& r, const void* act, const void* w2,
                                const float* topk_w, const int32_t* sorted_slots,
-                               const int32_t* tiles, const int32_t* num_tiles, void* slot_out,
-                               hipStream_t s) {
+                               const int32_t* offsets, const int32_t* tiles,
+                               const int32_t* num_tiles, void* slot_out, hipStream_t s) {
   pf::Args a{};
+  a.offsets = offsets;
   a.a_src = (const char*)act;
   a.w = (const char*)w2;
   a.sorted_slots = sorted_slots;

@@ -84,23 +84,25 @@ hipError_t launch_quant_rows(const Resolved& r, const void* x, uint8_t* xq, floa
                              hipStream_t s);
 
 hipError_t launch_up(const Resolved& r, const void* x, const float* x_scales, const void* w13,
-                     const float* w13_scales, const int32_t* sorted_slots, const int32_t* tiles,
-                     const int32_t* num_tiles, void* act, float* act_scales, hipStream_t s);
+                     const float* w13_scales, const int32_t* sorted_slots, const int32_t* offsets,
+                     const int32_t* tiles, const int32_t* num_tiles, void* act, float* act_scales,
+                     hipStream_t s);
 
 hipError_t launch_down(const Resolved& r, const void* act, const float* act_scales,
                        const void* w2, const float* w2_scales, const float* topk_w,
-                       const int32_t* sorted_slots, const int32_t* tiles,
+                       const int32_t* sorted_slots, const int32_t* offsets, const int32_t* tiles,
                        const int32_t* num_tiles, void* slot_out, hipStream_t s);
 
 // bf16 kernels for 128-row m-blocks (MFMA 32x32x16), used by launch_up / launch_down.
 bool prefill_supported(const Resolved& r);
 hipError_t launch_up_prefill(const Resolved& r, const void* x, const void* w13,
-                             const int32_t* sorted_slots, const int32_t* tiles,
-                             const int32_t* num_tiles, void* act, hipStream_t s);
+                             const int32_t* sorted_slots, const int32_t* offsets,
+                             const int32_t* tiles, const int32_t* num_tiles, void* act,
+                             hipStream_t s);
 hipError_t launch_down_prefill(const Resolved& r, const void* act, const void* w2,
                                const float* topk_w, const int32_t* sorted_slots,
-                               const int32_t* tiles, const int32_t* num_tiles, void* slot_out,
-                               hipStream_t s);
+                               const int32_t* offsets, const int32_t* tiles,
+                               const int32_t* num_tiles, void* slot_out, hipStream_t s);
 
 hipError_t launch_combine(const Resolved& r, const void* slot_out, const int32_t* slot_row,
                           void* out, hipStream_t s);

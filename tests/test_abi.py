@@ -72,15 +72,15 @@ def test_entry_points_reject_before_any_hip_call(lib):
     p = bad(H=100)
     P = ctypes.byref(p)
     assert lib.moe_align(P, *([None] * 9)) == moe.MOE_ERR_SHAPE
-    assert lib.moe_grouped_gemm_up(P, *([None] * 10)) == moe.MOE_ERR_SHAPE
-    assert lib.moe_grouped_gemm_down(P, *([None] * 10)) == moe.MOE_ERR_SHAPE
+    assert lib.moe_grouped_gemm_up(P, *([None] * 11)) == moe.MOE_ERR_SHAPE
+    assert lib.moe_grouped_gemm_down(P, *([None] * 11)) == moe.MOE_ERR_SHAPE
     assert lib.moe_combine(P, None, None, None, None) == moe.MOE_ERR_SHAPE
     assert lib.moe_forward(P, *([None] * 9), 0, None) == moe.MOE_ERR_SHAPE
     p = bad()
     P = ctypes.byref(p)
     assert lib.moe_align(P, *([None] * 9)) == moe.MOE_ERR_NULL
-    assert lib.moe_grouped_gemm_up(P, *([None] * 10)) == moe.MOE_ERR_NULL
-    assert lib.moe_grouped_gemm_down(P, *([None] * 10)) == moe.MOE_ERR_NULL
+    assert lib.moe_grouped_gemm_up(P, *([None] * 11)) == moe.MOE_ERR_NULL
+    assert lib.moe_grouped_gemm_down(P, *([None] * 11)) == moe.MOE_ERR_NULL
     assert lib.moe_combine(P, None, None, None, None) == moe.MOE_ERR_NULL
     assert lib.moe_quantize_rows_e4m3(P, 8, 8, 8, None) == moe.MOE_ERR_DTYPE   # bf16 weights
     fake = [ctypes.c_void_p(256)] * 9

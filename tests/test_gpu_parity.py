@@ -214,11 +214,11 @@ def test_stages_small(device, name, bm):
         x_in = torch.empty((cfg.T, cfg.H), dtype=torch.uint8, device=device)
         x_sc = torch.empty((cfg.T, cfg.H // 128), dtype=torch.float32, device=device)
         moe.moe_quantize_rows_e4m3(p, case.x, x_in, x_sc)
-    moe.moe_grouped_gemm_up(p, x_in, x_sc, case.w13, case.w13_scales, a["sorted_slots"], a["tiles"],
+    moe.moe_grouped_gemm_up(p, x_in, x_sc, case.w13, case.w13_scales, a["sorted_slots"], a["offsets"], a["tiles"],
                             a["num_tiles"], act, act_scales)
     slot_out = torch.full((cfg.T * cfg.top_k, cfg.H), float("nan"), dtype=case.x.dtype, device=device)
     moe.moe_grouped_gemm_down(p, act, act_scales, case.w2, case.w2_scales, case.topk_weights,
-                              a["sorted_slots"], a["tiles"], a["num_tiles"], slot_out)
+                              a["sorted_slots"], a["offsets"], a["tiles"], a["num_tiles"], slot_out)
     out = torch.empty((cfg.T, cfg.H), dtype=case.x.dtype, device=device)
     moe.moe_combine(p, slot_out, a["slot_row"], out)
     torch.cuda.synchronize()
