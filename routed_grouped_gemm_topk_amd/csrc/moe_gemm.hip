@@ -33,55 +33,6 @@
 
 namespace moe {
 
-// ---------------------------------------------------------------------------------------------
-// MFMA operand types
-// ---------------------------------------------------------------------------------------------
-struct OpBf16 {
-  static constexpr int ELT = 2;   // bytes per element
-  static constexpr int KPM = 32;  // k covered by one MFMA
-  static constexpr int LB = 16;   // operand bytes per lane
-  using frag = bf16x8;
-  __device__ static __forceinline__ frag load(const char* p) {
-    return *reinterpret_cast<const frag*>(p);
-  }
-  __device__ static __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-
-struct OpF32 {
-  static constexpr int ELT = 4;
-  static constexpr int KPM = 4;
-  static constexpr int LB = 4;
-  using frag = float;
-  __device__ static __forceinline__ frag load(const char* p) {
-    return *reinterpret_cast<const float*>(p);
-  }
-  __device__ static __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-  }
-};
-
-struct OpE4M3 {
-  static constexpr int ELT = 1;
-  static constexpr int KPM = 128;
-  static constexpr int LB = 32;
-  using frag = i32x8;
-  __device__ static __forceinline__ frag load(const char* p) {
-    const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
-    const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 16);
-    frag f;
-    f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
-    f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
-    return f;
-  }
-  // format 0 = e4m3 for both operands; E8M0 scale 127 = 1.0 (no MX scaling here)
-  __device__ static __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-  }
-};
-
-enum OutKind { OUT_F32 = 0, OUT_BF16 = 1, OUT_E4M3 = 2 };
 
 struct GemmArgs {
   const char* a_src;          // up: X or its e4m3 codes [T, K]; down: act [rows_max, K]
@@ -101,17 +52,6 @@ struct GemmArgs {
   int tiles_max;
   int64_t w_expert_elems;     // elements per expert weight slab
 };
-
-// Work split over the 8 XCDs: block b runs on XCD b % 8; each XCD takes a contiguous range
-// of the `valid` logical tiles (device-side tile count x n-blocks), so no XCD idles on the
-// slack between the host-side tile bound and the real count.  -1: nothing to do.
-__device__ __forceinline__ int xcd_logical(int b, int valid) {
-  const int per = (valid + 7) >> 3;
-  const int i = b >> 3;
-  if (i >= per) return -1;
-  const int l = (b & 7) * per + i;
-  return l < valid ? l : -1;
-}
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
   // SiLU(g) * u = g / (1 + exp(-g)) * u; exp(-g) = inf for very negative g gives -0.
@@ -431,6 +371,9 @@ hipError_t launch_up(const Resolved& r, const void* x, const float* x_scales, co
                      hipStream_t s) {
   if (prefill_supported(r))
     return launch_up_prefill(r, x, w13, sorted_slots, offsets, tiles, num_tiles, act, s);
+  if (stream_supported(r))
+    return launch_up_stream(r, x, x_scales, w13, w13_scales, sorted_slots, tiles, num_tiles, act,
+                            act_scales, s);
   GemmArgs a{};
   a.a_src = (const char*)x;
   a.a_scales = x_scales;
@@ -460,6 +403,9 @@ hipError_t launch_down(const Resolved& r, const void* act, const float* act_scal
   if (prefill_supported(r))
     return launch_down_prefill(r, act, w2, topk_w, sorted_slots, offsets, tiles, num_tiles,
                                slot_out, s);
+  if (stream_supported(r))
+    return launch_down_stream(r, act, act_scales, w2, w2_scales, topk_w, sorted_slots, tiles,
+                              num_tiles, slot_out, s);
   GemmArgs a{};
   a.a_src = (const char*)act;
   a.a_scales = act_scales;

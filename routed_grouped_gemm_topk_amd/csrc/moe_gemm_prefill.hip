@@ -46,18 +46,6 @@ __device__ __forceinline__ int swz(int r) {
   else return ((r >> 1) ^ (r >> 3)) & 3;
 }
 
-// Work split over the 8 XCDs (each with its own L2): workgroups are dispatched round-robin,
-// so block b runs on XCD b % 8.  Each XCD takes one contiguous range of the `valid` logical
-// tiles (valid = device-side tile count x n-blocks); blocks past their XCD's share exit.
-// Returns -1 for such blocks.
-__device__ __forceinline__ int xcd_logical(int b, int valid) {
-  const int per = (valid + 7) >> 3;
-  const int i = b >> 3;
-  if (i >= per) return -1;
-  const int l = (b & 7) * per + i;
-  return l < valid ? l : -1;
-}
-
 // Logical tile order, expert by expert: inside expert e (m-blocks base..base+M-1) groups of
 // GROUP_M m-blocks sweep the n-blocks, n-block-major inside a group.  A group never holds two
 // experts, so one XCD's concurrent workgroups share their weight tiles (each fetched once) and
@@ -316,16 +304,6 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_kernel(Args g) {
 // ring each k-slice.  The per-lane source address is chosen so that the fixed
 // lane -> LDS position mapping realises the same XOR swizzle as above.
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_addr)
-               : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 template <int BK, int NS, int BNA, bool UP>
 __global__ __launch_bounds__(4 * kWave) void gemm_dma_kernel(Args g) {
   constexpr int ROWB = BK * 2, KK = BK / 16, WN = 4;
@@ -429,13 +407,13 @@ __global__ __launch_bounds__(4 * kWave) void gemm_dma_kernel(Args g) {
       for (int j = 0; j < NF; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
   };
-  // One fragment read per MFMA while the reads last (hint to the scheduler).
+  // Scheduler hint: two MFMAs, then all of the next k-step's fragment reads back to back
+  // (one wave per SIMD needs many LDS reads in flight to cover LDS latency), then the rest
+  // of the MFMAs.
   auto interleave = [&]() {
-    #pragma unroll
-    for (int q = 0; q < FM * NF; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (q < FM + NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, FM + NF, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, FM * NF - 2, 0);
   };
   // k-step kk of the slice in `buf`: multiply set (kk & 1) while reading the next k-step
   // (of this slice, or k-step 0 of the slice in `nbuf`) into the other set.

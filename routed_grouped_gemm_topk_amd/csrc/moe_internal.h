@@ -65,6 +65,93 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// MFMA operand types
+// ---------------------------------------------------------------------------------------------
+struct OpBf16 {
+  static constexpr int ELT = 2;   // bytes per element
+  static constexpr int KPM = 32;  // k covered by one MFMA
+  static constexpr int LB = 16;   // operand bytes per lane
+  using frag = bf16x8;
+  __device__ static __forceinline__ frag load(const char* p) {
+    return *reinterpret_cast<const frag*>(p);
+  }
+  __device__ static __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+struct OpF32 {
+  static constexpr int ELT = 4;
+  static constexpr int KPM = 4;
+  static constexpr int LB = 4;
+  using frag = float;
+  __device__ static __forceinline__ frag load(const char* p) {
+    return *reinterpret_cast<const float*>(p);
+  }
+  __device__ static __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+struct OpE4M3 {
+  static constexpr int ELT = 1;
+  static constexpr int KPM = 128;
+  static constexpr int LB = 32;
+  using frag = i32x8;
+  __device__ static __forceinline__ frag load(const char* p) {
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 16);
+    frag f;
+    f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+    f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+    return f;
+  }
+  // format 0 = e4m3 for both operands; E8M0 scale 127 = 1.0 (no MX scaling here)
+  __device__ static __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
+enum OutKind { OUT_F32 = 0, OUT_BF16 = 1, OUT_E4M3 = 2 };
+
+// Work split over the 8 XCDs (each with its own L2): block b runs on XCD b % 8; each XCD
+// takes a contiguous range of the `valid` logical tiles (device-side tile count x n-blocks),
+// so no XCD idles on the slack between the host-side tile bound and the real count.  The
+// grid must be a multiple of 8 and at least `valid`.  -1: nothing to do for this block.
+__device__ __forceinline__ int xcd_logical(int b, int valid) {
+  const int per = (valid + 7) >> 3;
+  const int i = b >> 3;
+  if (i >= per) return -1;
+  const int l = (b & 7) * per + i;
+  return l < valid ? l : -1;
+}
+
+// Direct-to-LDS copies (gfx950 global_load_lds_dwordx4 / _dword): each wave instruction lands
+// 64 lanes x 16 (or 4) bytes contiguously in LDS at M0.  Issued from inline assembly with
+// explicit vmcnt waits: the compiler's own tracking of LDS DMA makes every LDS read wait for
+// every outstanding copy, which would drain a multi-stage ring each k-slice.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_addr)
+               : "memory");
+}
+
+__device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds_addr)
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+
+template <class T>
+__device__ __forceinline__ uint32_t lds_u32(T* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)p;
+}
+
+// ---------------------------------------------------------------------------------------------
 // Launchers (host side), one per translation unit
 // ---------------------------------------------------------------------------------------------
 struct Resolved {
@@ -103,6 +190,17 @@ hipError_t launch_down_prefill(const Resolved& r, const void* act, const void* w
                                const float* topk_w, const int32_t* sorted_slots,
                                const int32_t* offsets, const int32_t* tiles,
                                const int32_t* num_tiles, void* slot_out, hipStream_t s);
+
+// Weight-streaming kernels (bf16 m-blocks of 16..64 rows, e4m3 m-blocks of 128 rows).
+bool stream_supported(const Resolved& r);
+hipError_t launch_up_stream(const Resolved& r, const void* x, const float* x_scales,
+                            const void* w13, const float* w13_scales, const int32_t* sorted_slots,
+                            const int32_t* tiles, const int32_t* num_tiles, void* act,
+                            float* act_scales, hipStream_t s);
+hipError_t launch_down_stream(const Resolved& r, const void* act, const float* act_scales,
+                              const void* w2, const float* w2_scales, const float* topk_w,
+                              const int32_t* sorted_slots, const int32_t* tiles,
+                              const int32_t* num_tiles, void* slot_out, hipStream_t s);
 
 hipError_t launch_combine(const Resolved& r, const void* slot_out, const int32_t* slot_row,
                           void* out, hipStream_t s);
