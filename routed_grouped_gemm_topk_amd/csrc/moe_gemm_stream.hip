@@ -29,8 +29,7 @@ namespace moe {
 namespace st {
 
 constexpr int ROWB = 128;   // bytes per row per k-slice
-constexpr int WN = 4;       // waves, side by side along N
-constexpr int NT = WN * kWave;
+constexpr int WN = 4;       // waves side by side along N (times WM waves along M)
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
@@ -52,26 +51,30 @@ struct Args {
   int64_t w_expert_elems;
 };
 
-template <class Op, int BM, int BNA, int NS, bool UP, int OUT>
-__global__ __launch_bounds__(NT) void stream_kernel(Args g) {
+template <class Op, int BM, int BNA, int NS, bool UP, int OUT, int WM>
+__global__ __launch_bounds__(WN * WM * kWave) void stream_kernel(Args g) {
   constexpr bool SCALED = std::is_same<Op, OpE4M3>::value;
   constexpr int BK = ROWB / Op::ELT;             // values per row per slice
   constexpr int KK = BK / Op::KPM;               // MFMA k-steps per slice
   constexpr int STEPB = Op::KPM * Op::ELT;       // bytes per row per k-step
   constexpr int BROWS = UP ? 2 * BNA : BNA;
   constexpr int WTN = BNA / WN;
-  constexpr int FM = BM / 16;
+  constexpr int NW = WN * WM;                    // waves
+  constexpr int NT = NW * kWave;
+  constexpr int FM = BM / 16;                    // 16-row fragments of the m-block ...
+  constexpr int FMW = FM / WM;                   // ... of which wave row wm holds wm, wm+WM, ...
   constexpr int FN = WTN / 16;
   constexpr int NF = UP ? 2 * FN : FN;
   constexpr int NQ_REAL = (BM + BROWS) * ROWB / 1024;   // 1 KB copies (8 rows) per slice
-  constexpr int NQ = (NQ_REAL + WN - 1) / WN * WN;      // padded to whole waves
-  constexpr int NQW = NQ / WN;
+  constexpr int NQ = (NQ_REAL + NW - 1) / NW * NW;      // padded to whole waves
+  constexpr int NQW = NQ / NW;
   constexpr int SC_OFF = NQ * 1024;                     // row scales: one dword copy per wave
-  constexpr int STAGE = SC_OFF + (SCALED ? WN * 256 : 0);
+  constexpr int STAGE = SC_OFF + (SCALED ? NW * 256 : 0);
   constexpr int OPS = NQW + (SCALED ? 1 : 0);           // copies per wave per slice
   static_assert((BM + BROWS) % 8 == 0 && WTN % 16 == 0, "whole copies and MFMA tiles");
+  static_assert(FM % WM == 0, "fragments split evenly over the wave rows");
   static_assert(NS >= 2 && (NS - 1) * OPS <= 63, "vmcnt range");
-  static_assert(!SCALED || (KK == 1 && BNA == kGroup && BM <= WN * 64),
+  static_assert(!SCALED || (KK == 1 && BNA == kGroup && BM <= NW * 64),
                 "e4m3: one scale block per slice, one act group per tile");
   static_assert(Op::LB == 16 || Op::LB == 32, "16x16 fragments of one or two 16-byte chunks");
 
@@ -80,7 +83,8 @@ __global__ __launch_bounds__(NT) void stream_kernel(Args g) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int wn = wave;
+  const int wn = wave % WN;
+  const int wm = wave / WN;
 
   // ---- tile: n-block fastest.  At these block sizes an expert has about one m-block, so
   // workgroups share no weights; what they can share is the m-block's gathered A rows, which
@@ -184,9 +188,11 @@ __global__ __launch_bounds__(NT) void stream_kernel(Args g) {
     }
   };
 
-  f32x4 acc[FM][NF];
+  // acc[i]: fragment fi(i) = wm + WM * i of the m-block, rows fi(i) * 16 + [0, 16)
+  auto fi = [&](int i) { return wm + WM * i; };
+  f32x4 acc[FMW][NF];
   #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FMW; ++i)
     #pragma unroll
     for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -208,6 +214,16 @@ __global__ __launch_bounds__(NT) void stream_kernel(Args g) {
         sws[1][i] = sw_up[i];
       }
     }
+    // An m-block holds its expert's rows first and padding after, so 16-row fragments from
+    // ceil(valid / 16) on are all padding: their products are skipped (accumulators stay 0).
+    int fmv;
+    {
+      const int s_lo = g.sorted_slots[row0 + min(lane, BM - 1)];
+      const int s_hi = g.sorted_slots[row0 + min(lane + kWave, BM - 1)];
+      const int valid = __popcll(__ballot(lane < BM && s_lo < g.n_slots)) +
+                        __popcll(__ballot(lane + kWave < BM && s_hi < g.n_slots));
+      fmv = __builtin_amdgcn_readfirstlane((valid + 15) >> 4);
+    }
     #pragma unroll
     for (int s = 0; s < NS - 1; ++s) issue(s, min(s, KT - 1));
     int buf = 0;
@@ -223,16 +239,18 @@ __global__ __launch_bounds__(NT) void stream_kernel(Args g) {
       for (int j = 0; j < NF; ++j) bf[j] = load_frag(stg + b_row[j], 0);
       // every product of the slice first (independent MFMAs back to back), then the scaled
       // accumulation, so no MFMA result is waited for inside the MFMA sequence
-      f32x4 part[FM][NF];
+      f32x4 part[FMW][NF];
       #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const frag af = load_frag(stg + i * 16 * ROWB, 0);
+      for (int i = 0; i < FMW; ++i) {
+        if (fi(i) >= fmv) break;
+        const frag af = load_frag(stg + fi(i) * 16 * ROWB, 0);
         #pragma unroll
         for (int j = 0; j < NF; ++j) part[i][j] = Op::mma(af, bf[j], f32x4{0.f, 0.f, 0.f, 0.f});
       }
       #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const f32x4 sa = *reinterpret_cast<const f32x4*>(sc + i * 16 + (lane >> 4) * 4);
+      for (int i = 0; i < FMW; ++i) {
+        if (fi(i) >= fmv) break;
+        const f32x4 sa = *reinterpret_cast<const f32x4*>(sc + fi(i) * 16 + (lane >> 4) * 4);
         #pragma unroll
         for (int j = 0; j < NF; ++j) {
           const float sw = (UP && j >= FN) ? sw_u : sw_g;
@@ -244,17 +262,17 @@ __global__ __launch_bounds__(NT) void stream_kernel(Args g) {
     }
     wait_vmcnt<0>();
   } else {
-    frag a0[FM], b0[NF], a1[FM], b1[NF];
+    frag a0[FMW], b0[NF], a1[FMW], b1[NF];
     auto read_frags = [&](frag* af, frag* bfr, int buf, int kk) {
       const char* stg = lds + buf * STAGE;
       #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = load_frag(stg + i * 16 * ROWB, kk);
+      for (int i = 0; i < FMW; ++i) af[i] = load_frag(stg + fi(i) * 16 * ROWB, kk);
       #pragma unroll
       for (int j = 0; j < NF; ++j) bfr[j] = load_frag(stg + b_row[j], kk);
     };
     auto mfmas = [&](const frag* af, const frag* bfr) {
       #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FMW; ++i)
         #pragma unroll
         for (int j = 0; j < NF; ++j) acc[i][j] = Op::mma(af[i], bfr[j], acc[i][j]);
     };
@@ -295,9 +313,9 @@ __global__ __launch_bounds__(NT) void stream_kernel(Args g) {
   const int ocol = lane & 15;
   const int orow = (lane >> 4) * 4;
   if constexpr (UP) {
-    float a[FM][FN][4];
+    float a[FMW][FN][4];
     #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FMW; ++i)
       #pragma unroll
       for (int j = 0; j < FN; ++j)
         #pragma unroll
@@ -310,7 +328,7 @@ __global__ __launch_bounds__(NT) void stream_kernel(Args g) {
       __syncthreads();                                   // LDS is free: the ring is drained
       float* red = reinterpret_cast<float*>(lds);
       #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FMW; ++i)
         #pragma unroll
         for (int v = 0; v < 4; ++v) {
           float m = 0.0f;
@@ -318,15 +336,15 @@ __global__ __launch_bounds__(NT) void stream_kernel(Args g) {
           for (int j = 0; j < FN; ++j) m = fmaxf(m, fabsf(a[i][j][v]));
           #pragma unroll
           for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
-          if (ocol == 0) red[wn * BM + i * 16 + orow + v] = m;
+          if (ocol == 0) red[wn * BM + fi(i) * 16 + orow + v] = m;
         }
       __syncthreads();
       uint8_t* act = reinterpret_cast<uint8_t*>(g.out);
       #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FMW; ++i)
         #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int m = i * 16 + orow + v;
+          const int m = fi(i) * 16 + orow + v;
           float amax = 0.0f;
           #pragma unroll
           for (int w = 0; w < WN; ++w) amax = fmaxf(amax, red[w * BM + m]);
@@ -340,29 +358,29 @@ __global__ __launch_bounds__(NT) void stream_kernel(Args g) {
         }
     } else {
       #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FMW; ++i)
         #pragma unroll
         for (int v = 0; v < 4; ++v) {
           uint16_t* dst = reinterpret_cast<uint16_t*>(g.out) +
-                          (size_t)(row0 + i * 16 + orow + v) * g.n_out + n0 + wn * WTN + ocol;
+                          (size_t)(row0 + fi(i) * 16 + orow + v) * g.n_out + n0 + wn * WTN + ocol;
           #pragma unroll
           for (int j = 0; j < FN; ++j) dst[j * 16] = (uint16_t)f32_to_bf16_bits(a[i][j][v]);
         }
     }
   } else {
     // slots, then routing weights, each batch of loads under one wait
-    int sl[FM][4];
-    float wt_[FM][4];
+    int sl[FMW][4];
+    float wt_[FMW][4];
     #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FMW; ++i)
       #pragma unroll
-      for (int v = 0; v < 4; ++v) sl[i][v] = g.sorted_slots[row0 + i * 16 + orow + v];
+      for (int v = 0; v < 4; ++v) sl[i][v] = g.sorted_slots[row0 + fi(i) * 16 + orow + v];
     #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FMW; ++i)
       #pragma unroll
       for (int v = 0; v < 4; ++v) wt_[i][v] = g.topk_w[min(sl[i][v], g.n_slots - 1)];
     #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FMW; ++i)
       #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int s = sl[i][v];
@@ -375,21 +393,21 @@ __global__ __launch_bounds__(NT) void stream_kernel(Args g) {
   }
 }
 
-template <class Op, int BM, int BNA, int NS, bool UP, int OUT>
+template <class Op, int BM, int BNA, int NS, bool UP, int OUT, int WM = 1>
 hipError_t run(const Args& a, hipStream_t s) {
   const int64_t grid = ((int64_t)a.tiles_max * (a.n_out / BNA) + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((stream_kernel<Op, BM, BNA, NS, UP, OUT>), dim3((unsigned)grid), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((stream_kernel<Op, BM, BNA, NS, UP, OUT, WM>), dim3((unsigned)grid),
+                     dim3(WN * WM * kWave), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace st
 
-// bf16 with 16..64-row m-blocks, and e4m3 with 128-row m-blocks.
+// bf16 with 16..64-row m-blocks, and e4m3 with any m-block size.
 bool stream_supported(const Resolved& r) {
   if (r.w_dtype == MOE_BF16) return r.BM <= 64;
-  if (r.w_dtype == MOE_E4M3) return r.BM == 128;
-  return false;
+  return r.w_dtype == MOE_E4M3;
 }
 
 hipError_t launch_up_stream(const Resolved& r, const void* x, const float* x_scales,
@@ -412,7 +430,14 @@ hipError_t launch_up_stream(const Resolved& r, const void* x, const float* x_sca
   a.n_slots = (int)r.N;
   a.tiles_max = (int)r.tiles_max;
   a.w_expert_elems = (int64_t)2 * r.I * r.H;
-  if (r.w_dtype == MOE_E4M3) return st::run<OpE4M3, 128, 128, 3, true, OUT_E4M3>(a, s);
+  if (r.w_dtype == MOE_E4M3) {
+    switch (r.BM) {
+      case 16: return st::run<OpE4M3, 16, 128, 3, true, OUT_E4M3>(a, s);
+      case 32: return st::run<OpE4M3, 32, 128, 3, true, OUT_E4M3, 2>(a, s);
+      case 64: return st::run<OpE4M3, 64, 128, 3, true, OUT_E4M3, 2>(a, s);
+      default: return st::run<OpE4M3, 128, 128, 3, true, OUT_E4M3, 2>(a, s);
+    }
+  }
   switch (r.BM) {
     case 16: return st::run<OpBf16, 16, 128, 4, true, OUT_BF16>(a, s);
     case 32: return st::run<OpBf16, 32, 128, 4, true, OUT_BF16>(a, s);
@@ -440,7 +465,14 @@ hipError_t launch_down_stream(const Resolved& r, const void* act, const float* a
   a.n_slots = (int)r.N;
   a.tiles_max = (int)r.tiles_max;
   a.w_expert_elems = (int64_t)r.H * r.I;
-  if (r.w_dtype == MOE_E4M3) return st::run<OpE4M3, 128, 128, 4, false, OUT_BF16>(a, s);
+  if (r.w_dtype == MOE_E4M3) {
+    switch (r.BM) {
+      case 16: return st::run<OpE4M3, 16, 128, 4, false, OUT_BF16>(a, s);
+      case 32: return st::run<OpE4M3, 32, 128, 4, false, OUT_BF16, 2>(a, s);
+      case 64: return st::run<OpE4M3, 64, 128, 4, false, OUT_BF16, 2>(a, s);
+      default: return st::run<OpE4M3, 128, 128, 4, false, OUT_BF16, 2>(a, s);
+    }
+  }
   if (r.H % 256 == 0) {
     switch (r.BM) {
       case 16: return st::run<OpBf16, 16, 256, 4, false, OUT_BF16>(a, s);
