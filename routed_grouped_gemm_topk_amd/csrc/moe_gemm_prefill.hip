@@ -304,20 +304,20 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_kernel(Args g) {
 // ring each k-slice.  The per-lane source address is chosen so that the fixed
 // lane -> LDS position mapping realises the same XOR swizzle as above.
 // ---------------------------------------------------------------------------------------------
-template <int BK, int NS, int BNA, bool UP>
-__global__ __launch_bounds__(4 * kWave) void gemm_dma_kernel(Args g) {
-  constexpr int ROWB = BK * 2, KK = BK / 16, WN = 4;
+template <int BK, int NS, int BNA, bool UP, int WM>
+__global__ __launch_bounds__(4 * WM * kWave) void gemm_dma_kernel(Args g) {
+  constexpr int ROWB = BK * 2, KK = BK / 16, WN = 4, NW = WN * WM;
   constexpr int BROWS = UP ? 2 * BNA : BNA;
   constexpr int WTN = BNA / WN;
-  constexpr int FM = BM / 32;
+  constexpr int FM = BM / 32 / WM;                // 32-row fragments per wave (rows wm*BM/WM ...)
   constexpr int FN = WTN / 32;
   constexpr int NF = UP ? 2 * FN : FN;
   constexpr int STAGE = (BM + BROWS) * ROWB;
   constexpr int NQ = STAGE / 1024;                // 1 KB wave copies per slice
-  constexpr int NQW = NQ / WN;                    // per wave
+  constexpr int NQW = NQ / NW;                    // per wave
   constexpr int ROWS_PER_Q = 1024 / ROWB;
   constexpr int CPR = ROWB / 16;
-  static_assert(NQ % WN == 0, "copies split evenly over the waves");
+  static_assert(NQ % NW == 0, "copies split evenly over the waves");
   static_assert(NS >= 2 && (NS - 1) * NQW <= 63, "vmcnt range");
 
   __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
@@ -325,7 +325,9 @@ __global__ __launch_bounds__(4 * kWave) void gemm_dma_kernel(Args g) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int wn = wave;
+  const int wn = wave % WN;
+  const int wm = wave / WN;
+  const int mrow0 = wm * (BM / WM);               // this wave's first row of the m-block
 
   const int nblk = g.n_out / BNA;
   const int logical = xcd_logical(blockIdx.x, *g.num_tiles * nblk);
@@ -396,7 +398,7 @@ __global__ __launch_bounds__(4 * kWave) void gemm_dma_kernel(Args g) {
   auto read_frags = [&](bf16x8* af, bf16x8* bfr, int buf, int kk) {
     const char* st = lds + buf * STAGE;
     #pragma unroll
-    for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(st + i * 32 * ROWB + lane_off[kk]);
+    for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(st + (mrow0 + i * 32) * ROWB + lane_off[kk]);
     #pragma unroll
     for (int j = 0; j < NF; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(st + b_row[j] + lane_off[kk]);
   };
@@ -459,7 +461,7 @@ __global__ __launch_bounds__(4 * kWave) void gemm_dma_kernel(Args g) {
     for (int i = 0; i < FM; ++i)
       #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = i * 32 + 8 * (v >> 2) + orow + (v & 3);
+        const int m = mrow0 + i * 32 + 8 * (v >> 2) + orow + (v & 3);
         uint16_t* dst = g.out + (size_t)(row0 + m) * g.n_out + n0 + wn * WTN + ocol;
         #pragma unroll
         for (int j = 0; j < FN; ++j) {
@@ -473,7 +475,7 @@ __global__ __launch_bounds__(4 * kWave) void gemm_dma_kernel(Args g) {
     for (int i = 0; i < FM; ++i)
       #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = i * 32 + 8 * (v >> 2) + orow + (v & 3);
+        const int m = mrow0 + i * 32 + 8 * (v >> 2) + orow + (v & 3);
         const int s = g.sorted_slots[row0 + m];
         if (s >= g.n_slots) continue;
         const float wt = g.topk_w[s];
@@ -484,12 +486,13 @@ __global__ __launch_bounds__(4 * kWave) void gemm_dma_kernel(Args g) {
   }
 }
 
-template <int BK, int NS, int BNA, bool UP>
+template <int BK, int NS, int BNA, bool UP, int WM = 1>
 hipError_t run_dma(const Args& a, hipStream_t s) {
   // multiple of 8: every XCD's share of the valid tiles must have blocks to run on
   const int64_t grid = ((int64_t)a.tiles_max * (a.n_out / BNA) + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_dma_kernel<BK, NS, BNA, UP>), dim3((unsigned)grid), dim3(4 * kWave), 0, s, a);
+  hipLaunchKernelGGL((gemm_dma_kernel<BK, NS, BNA, UP, WM>), dim3((unsigned)grid),
+                     dim3(4 * WM * kWave), 0, s, a);
   return hipGetLastError();
 }
 
@@ -527,7 +530,7 @@ hipError_t launch_up_prefill(const Resolved& r, const void* x, const void* w13,
   a.n_slots = (int)r.N;
   a.tiles_max = (int)r.tiles_max;
   a.w_expert_elems = (int64_t)2 * r.I * r.H;
-  if (r.I % 256 == 0) return pf::run_dma<64, 2, 256, true>(a, s);
+  if (r.I % 256 == 0) return pf::run_dma<64, 2, 256, true, 2>(a, s);
   return pf::run_dma<64, 3, 128, true>(a, s);
 }
 
@@ -550,7 +553,7 @@ hipError_t launch_down_prefill(const Resolved& r, const void* act, const void* w
   a.n_slots = (int)r.N;
   a.tiles_max = (int)r.tiles_max;
   a.w_expert_elems = (int64_t)r.H * r.I;
-  if (r.H % 256 == 0) return pf::run_dma<64, 3, 256, false>(a, s);
+  if (r.H % 256 == 0) return pf::run_dma<64, 3, 256, false, 2>(a, s);
   return pf::run_dma<64, 4, 128, false>(a, s);
 }
 
