@@ -81,6 +81,12 @@ def adversarial():
     yield "id_equal_E", np.array([[0, 6], [6, 1], [5, 6]], np.int32), 6
     yield "many_chunks_E1024", rng.integers(0, 1024, (3000, 8)).astype(np.int32), 1024
     yield "E1", np.zeros((77, 1), np.int32), 1
+    # chunked path (more than 8192 slots): ragged last chunk, invalid ids, one hot expert
+    yield "chunks_ragged_invalid", np.where(rng.random((5003, 3)) < 0.1, 40,
+                                            rng.integers(0, 40, (5003, 3))).astype(np.int32), 40
+    yield "chunks_just_above_limit", np.full((4100, 2), 3, np.int32), 8
+    yield "small_path_at_limit", rng.integers(0, 8, (4096, 2)).astype(np.int32), 8
+    yield "chunks_skewed", np.minimum((64 * rng.random((9000, 6)) ** 3).astype(np.int32), 63), 64
 
 
 @pytest.mark.parametrize("name,ids,E", list(adversarial()), ids=lambda v: v if isinstance(v, str) else "")
