@@ -65,7 +65,8 @@ typedef enum moe_dtype {
  * Limits: 1 <= top_k <= E <= 1024; T >= 1; H and I multiples of 128, at most 32768;
  *         T*top_k < 2^31 and per-expert weight slabs < 2^31 bytes.
  * block_m: rows per m-block of the expert-sorted slot list, one of 16, 32, 64,
- *          128; 0 lets the library choose (moe_pick_block_m).  Every entry point
+ *          128, or 256 (bf16 problems only); 0 lets the library choose
+ *          (moe_pick_block_m).  Every entry point
  *          resolves 0 the same way, so the same moe_problem describes all stages.
  */
 typedef struct moe_problem {

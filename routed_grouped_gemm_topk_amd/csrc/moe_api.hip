@@ -21,11 +21,14 @@ int32_t choose_block_m(const moe_problem* p) {
   if (p->block_m) return p->block_m;
   // Expected slots per expert, m = T*top_k/E.  Few slots per expert: the m-block
   // should hold a whole expert so each weight tile is streamed from HBM once;
-  // many slots: 128-row blocks keep the MFMA tiles large.
+  // many slots: large m-blocks keep the MFMA tiles large.  bf16 experts with hundreds
+  // of slots take 256-row blocks (fewer bytes per flop through LDS; the extra padding
+  // of an expert's last block is at most 255 rows).
   const double m = (double)p->T * p->top_k / p->E;
   if (m <= 8) return 16;
   if (m <= 20) return 32;
   if (m <= 40) return 64;
+  if (m >= 512 && p->dtype == MOE_BF16 && p->w_dtype == MOE_BF16) return 256;
   return 128;
 }
 
@@ -35,12 +38,13 @@ int validate(const moe_problem* p) {
   if (p->H < 128 || p->I < 128 || p->H % 128 || p->I % 128) return MOE_ERR_SHAPE;
   if (p->H > kMaxDim || p->I > kMaxDim) return MOE_ERR_SHAPE;
   if (p->block_m != 0 && p->block_m != 16 && p->block_m != 32 && p->block_m != 64 &&
-      p->block_m != 128)
+      p->block_m != 128 && p->block_m != 256)
     return MOE_ERR_SHAPE;
   const bool f32 = p->dtype == MOE_F32 && p->w_dtype == MOE_F32;
   const bool bf16 = p->dtype == MOE_BF16 && p->w_dtype == MOE_BF16;
   const bool fp8 = p->dtype == MOE_BF16 && p->w_dtype == MOE_E4M3;
   if (!(f32 || bf16 || fp8)) return MOE_ERR_DTYPE;
+  if (p->block_m == 256 && !bf16) return MOE_ERR_SHAPE;     // 256-row blocks: bf16 only
   const int64_t N = (int64_t)p->T * p->top_k;
   const int64_t BM = choose_block_m(p);
   const int64_t rows = N + (int64_t)(p->E < N ? p->E : N) * (BM - 1);

@@ -50,11 +50,12 @@ __device__ __forceinline__ int swz(int r) {
 // GROUP_M m-blocks sweep the n-blocks, n-block-major inside a group.  A group never holds two
 // experts, so one XCD's concurrent workgroups share their weight tiles (each fetched once) and
 // their gathered rows.  logical / n_blocks is an m-block of the expert that owns `logical`.
+template <int BMT>
 __device__ __forceinline__ void tile_of(int logical, int n_blocks, const int32_t* tiles,
                                         const int32_t* offsets, int& mt, int& nt) {
   const int e = tiles[2 * (logical / n_blocks)];
-  const int base = offsets[e] / BM;
-  const int M = (offsets[e + 1] - offsets[e]) / BM;
+  const int base = offsets[e] / BMT;
+  const int M = (offsets[e + 1] - offsets[e]) / BMT;
   const int r = logical - base * n_blocks;          // 0 <= r < M * n_blocks
   const int full = M / GROUP_M;
   if (r < full * GROUP_M * n_blocks) {
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_kernel(Args g) {
   const int logical = xcd_logical(blockIdx.x, *g.num_tiles * nblk);
   if (logical < 0) return;
   int mt, nt;
-  tile_of(logical, nblk, g.tiles, g.offsets, mt, nt);
+  tile_of<BM>(logical, nblk, g.tiles, g.offsets, mt, nt);
   const int e = g.tiles[2 * mt];
   const int row0 = g.tiles[2 * mt + 1];
   const int n0 = nt * BNA;
@@ -304,15 +305,15 @@ __global__ __launch_bounds__(WM* WN* kWave) void gemm_kernel(Args g) {
 // ring each k-slice.  The per-lane source address is chosen so that the fixed
 // lane -> LDS position mapping realises the same XOR swizzle as above.
 // ---------------------------------------------------------------------------------------------
-template <int BK, int NS, int BNA, bool UP, int WM>
-__global__ __launch_bounds__(4 * WM * kWave) void gemm_dma_kernel(Args g) {
-  constexpr int ROWB = BK * 2, KK = BK / 16, WN = 4, NW = WN * WM;
+template <int BMT, int BK, int NS, int BNA, bool UP, int WM, int WN>
+__global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
+  constexpr int ROWB = BK * 2, KK = BK / 16, NW = WN * WM;
   constexpr int BROWS = UP ? 2 * BNA : BNA;
   constexpr int WTN = BNA / WN;
-  constexpr int FM = BM / 32 / WM;                // 32-row fragments per wave (rows wm*BM/WM ...)
+  constexpr int FM = BMT / 32 / WM;                // 32-row fragments per wave (rows wm*BMT/WM ...)
   constexpr int FN = WTN / 32;
   constexpr int NF = UP ? 2 * FN : FN;
-  constexpr int STAGE = (BM + BROWS) * ROWB;
+  constexpr int STAGE = (BMT + BROWS) * ROWB;
   constexpr int NQ = STAGE / 1024;                // 1 KB wave copies per slice
   constexpr int NQW = NQ / NW;                    // per wave
   constexpr int ROWS_PER_Q = 1024 / ROWB;
@@ -327,13 +328,13 @@ __global__ __launch_bounds__(4 * WM * kWave) void gemm_dma_kernel(Args g) {
   const int wave = tid / kWave;
   const int wn = wave % WN;
   const int wm = wave / WN;
-  const int mrow0 = wm * (BM / WM);               // this wave's first row of the m-block
+  const int mrow0 = wm * (BMT / WM);               // this wave's first row of the m-block
 
   const int nblk = g.n_out / BNA;
   const int logical = xcd_logical(blockIdx.x, *g.num_tiles * nblk);
   if (logical < 0) return;
   int mt, nt;
-  tile_of(logical, nblk, g.tiles, g.offsets, mt, nt);
+  tile_of<BMT>(logical, nblk, g.tiles, g.offsets, mt, nt);
   const int e = g.tiles[2 * mt];
   const int row0 = g.tiles[2 * mt + 1];
   const int n0 = nt * BNA;
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(4 * WM * kWave) void gemm_dma_kernel(Args g) {
     const int q = wave * NQW + i;
     const int r = q * ROWS_PER_Q + lane / CPR;      // row of the stage this lane fills
     const int cc = (lane % CPR) ^ swz<ROWB>(r);      // chunk that belongs at this position
-    if (r < BM) {
+    if (r < BMT) {
       if (UP) {
         const int s = g.sorted_slots[row0 + r];
         src[i] = (s < g.n_slots) ? g.a_src + (size_t)(s / g.top_k) * K * 2 + cc * 16
@@ -357,7 +358,7 @@ __global__ __launch_bounds__(4 * WM * kWave) void gemm_dma_kernel(Args g) {
         src[i] = g.a_src + (size_t)(row0 + r) * K * 2 + cc * 16;
       }
     } else {
-      const int rb = r - BM;
+      const int rb = r - BMT;
       const int grow = UP ? (rb < BNA ? n0 + rb : g.n_out + n0 + (rb - BNA)) : n0 + rb;
       src[i] = wbase + (size_t)grow * K * 2 + cc * 16;
     }
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(4 * WM * kWave) void gemm_dma_kernel(Args g) {
   for (int j = 0; j < NF; ++j) {
     const int r = UP ? ((j < FN) ? wn * WTN + j * 32 : BNA + wn * WTN + (j - FN) * 32)
                      : wn * WTN + j * 32;
-    b_row[j] = (BM + r) * ROWB;
+    b_row[j] = (BMT + r) * ROWB;
   }
 
   f32x16 acc[FM][NF];
@@ -486,13 +487,13 @@ __global__ __launch_bounds__(4 * WM * kWave) void gemm_dma_kernel(Args g) {
   }
 }
 
-template <int BK, int NS, int BNA, bool UP, int WM = 1>
+template <int BK, int NS, int BNA, bool UP, int WM = 1, int BMT = BM, int WN = 4>
 hipError_t run_dma(const Args& a, hipStream_t s) {
   // multiple of 8: every XCD's share of the valid tiles must have blocks to run on
   const int64_t grid = ((int64_t)a.tiles_max * (a.n_out / BNA) + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_dma_kernel<BK, NS, BNA, UP, WM>), dim3((unsigned)grid),
-                     dim3(4 * WM * kWave), 0, s, a);
+  hipLaunchKernelGGL((gemm_dma_kernel<BMT, BK, NS, BNA, UP, WM, WN>), dim3((unsigned)grid),
+                     dim3(WN * WM * kWave), 0, s, a);
   return hipGetLastError();
 }
 
@@ -508,8 +509,9 @@ hipError_t run(const Args& a, hipStream_t s) {
 
 }  // namespace pf
 
+// bf16 with 128- or 256-row m-blocks.
 bool prefill_supported(const Resolved& r) {
-  return r.w_dtype == MOE_BF16 && r.BM == pf::BM;
+  return r.w_dtype == MOE_BF16 && (r.BM == pf::BM || r.BM == 2 * pf::BM);
 }
 
 hipError_t launch_up_prefill(const Resolved& r, const void* x, const void* w13,
@@ -530,6 +532,8 @@ hipError_t launch_up_prefill(const Resolved& r, const void* x, const void* w13,
   a.n_slots = (int)r.N;
   a.tiles_max = (int)r.tiles_max;
   a.w_expert_elems = (int64_t)2 * r.I * r.H;
+  // 256-row m-blocks: 8 waves, 4 along M (64 rows each) x 2 along N
+  if (r.BM == 256) return pf::run_dma<64, 2, 128, true, 4, 256, 2>(a, s);
   if (r.I % 256 == 0) return pf::run_dma<64, 2, 256, true, 2>(a, s);
   return pf::run_dma<64, 3, 128, true>(a, s);
 }
@@ -553,6 +557,10 @@ hipError_t launch_down_prefill(const Resolved& r, const void* act, const void* w
   a.n_slots = (int)r.N;
   a.tiles_max = (int)r.tiles_max;
   a.w_expert_elems = (int64_t)r.H * r.I;
+  if (r.BM == 256) {
+    if (r.H % 256 == 0) return pf::run_dma<64, 2, 256, false, 4, 256, 2>(a, s);
+    return pf::run_dma<64, 2, 128, false, 4, 256, 2>(a, s);
+  }
   if (r.H % 256 == 0) return pf::run_dma<64, 3, 256, false, 2>(a, s);
   return pf::run_dma<64, 4, 128, false>(a, s);
 }

@@ -49,7 +49,8 @@ def bad(**kw):
     (dict(T=0), moe.MOE_ERR_SHAPE), (dict(H=100), moe.MOE_ERR_SHAPE), (dict(I=192), moe.MOE_ERR_SHAPE),
     (dict(E=0), moe.MOE_ERR_SHAPE), (dict(E=1025, top_k=2), moe.MOE_ERR_SHAPE),
     (dict(top_k=0), moe.MOE_ERR_SHAPE), (dict(top_k=9), moe.MOE_ERR_SHAPE),
-    (dict(block_m=48), moe.MOE_ERR_SHAPE), (dict(block_m=256), moe.MOE_ERR_SHAPE),
+    (dict(block_m=48), moe.MOE_ERR_SHAPE), (dict(block_m=512), moe.MOE_ERR_SHAPE),
+    (dict(block_m=256, dtype="f32"), moe.MOE_ERR_SHAPE), (dict(block_m=256, w_dtype="e4m3"), moe.MOE_ERR_SHAPE),
     (dict(dtype="f32", w_dtype="bf16"), moe.MOE_ERR_DTYPE), (dict(dtype="e4m3"), moe.MOE_ERR_DTYPE),
     (dict(dtype="f32", w_dtype="e4m3"), moe.MOE_ERR_DTYPE),
     (dict(H=2 ** 15 + 128), moe.MOE_ERR_SHAPE),                  # above the largest H
@@ -92,8 +93,9 @@ def test_entry_points_reject_before_any_hip_call(lib):
 
 
 @pytest.mark.parametrize("T,H,I,E,k,dt,wdt,bm", [
-    (16, 128, 256, 8, 2, "f32", "f32", 16), (4096, 4096, 14336, 8, 2, "bf16", "bf16", 128),
-    (64, 7168, 2048, 256, 8, "bf16", "bf16", 16), (8192, 2048, 1408, 64, 6, "bf16", "bf16", 128),
+    (16, 128, 256, 8, 2, "f32", "f32", 16), (4096, 4096, 14336, 8, 2, "bf16", "bf16", 256),
+    (64, 7168, 2048, 256, 8, "bf16", "bf16", 16), (8192, 2048, 1408, 64, 6, "bf16", "bf16", 256),
+    (2048, 4096, 1024, 8, 1, "bf16", "bf16", 128), (4096, 4096, 1024, 8, 1, "f32", "f32", 128),
     (2048, 7168, 2048, 256, 8, "bf16", "e4m3", 128), (1, 128, 128, 4, 1, "bf16", "bf16", 16),
 ])
 def test_block_m_choice_and_bounds(T, H, I, E, k, dt, wdt, bm):
@@ -101,7 +103,7 @@ def test_block_m_choice_and_bounds(T, H, I, E, k, dt, wdt, bm):
     assert moe.moe_pick_block_m(p) == bm
     assert moe.moe_max_padded_slots(p) == oracle.max_padded_slots(T * k, E, bm)
     assert moe.moe_max_tiles(p) == oracle.max_tiles(T * k, E, bm)
-    for forced in (16, 32, 64, 128):
+    for forced in (16, 32, 64, 128) + ((256,) if dt == wdt == "bf16" else ()):
         q = moe.make_problem(T, H, I, E, k, dt, wdt, block_m=forced)
         assert moe.moe_pick_block_m(q) == forced
         assert moe.moe_max_tiles(q) == oracle.max_tiles(T * k, E, forced)
