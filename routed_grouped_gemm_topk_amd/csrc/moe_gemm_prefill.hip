@@ -26,6 +26,8 @@
 //   * tile order: expert by expert, groups of 8 m-blocks of one expert sweep the n-blocks,
 //     and each XCD (own L2) runs a contiguous range of that order, so concurrent workgroups
 //     share rows and weights and each weight tile leaves HBM about once.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -394,65 +396,87 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
       #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
+  // Rows of the m-block that hold slots come first, padding after: this wave's 32-row
+  // fragments from fmv on are all padding, and their reads and MFMAs are skipped.
+  int fmv;
+  {
+    int valid = 0;
+    #pragma unroll
+    for (int r0 = 0; r0 < BMT; r0 += kWave)
+      valid += __popcll(__ballot(g.sorted_slots[row0 + r0 + lane] < g.n_slots));
+    fmv = __builtin_amdgcn_readfirstlane(min(FM, max(0, (valid - mrow0 + 31) / 32)));
+  }
+
   // Two fragment sets: one being multiplied, one being read.
   bf16x8 a0[FM], b0[NF], a1[FM], b1[NF];
-  auto read_frags = [&](bf16x8* af, bf16x8* bfr, int buf, int kk) {
-    const char* st = lds + buf * STAGE;
-    #pragma unroll
-    for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(st + (mrow0 + i * 32) * ROWB + lane_off[kk]);
-    #pragma unroll
-    for (int j = 0; j < NF; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(st + b_row[j] + lane_off[kk]);
-  };
-  auto mfmas = [&](const bf16x8* af, const bf16x8* bfr) {
-    #pragma unroll
-    for (int i = 0; i < FM; ++i)
+  // PARTIAL: some of this wave's fragments are padding (checked per fragment, no schedule hint)
+  auto main_loop = [&](auto partial_tag) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
+    auto read_frags = [&](bf16x8* af, bf16x8* bfr, int buf, int kk) {
+      const char* st = lds + buf * STAGE;
       #pragma unroll
-      for (int j = 0; j < NF; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-  };
-  // Scheduler hint: two MFMAs, then all of the next k-step's fragment reads back to back
-  // (one wave per SIMD needs many LDS reads in flight to cover LDS latency), then the rest
-  // of the MFMAs.
-  auto interleave = [&]() {
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, FM + NF, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, FM * NF - 2, 0);
-  };
-  // k-step kk of the slice in `buf`: multiply set (kk & 1) while reading the next k-step
-  // (of this slice, or k-step 0 of the slice in `nbuf`) into the other set.
-  auto step = [&](int kk, int buf, int nbuf) {
-    const int nb = (kk + 1 < KK) ? buf : nbuf;
-    const int nk = (kk + 1 < KK) ? kk + 1 : 0;
-    if (kk & 1) { read_frags(a0, b0, nb, nk); mfmas(a1, b1); }
-    else        { read_frags(a1, b1, nb, nk); mfmas(a0, b0); }
-    interleave();
-  };
+      for (int i = 0; i < FM; ++i)
+        if (!PARTIAL || i < fmv)
+          af[i] = *reinterpret_cast<const bf16x8*>(st + (mrow0 + i * 32) * ROWB + lane_off[kk]);
+      if (PARTIAL && fmv == 0) return;
+      #pragma unroll
+      for (int j = 0; j < NF; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(st + b_row[j] + lane_off[kk]);
+    };
+    auto mfmas = [&](const bf16x8* af, const bf16x8* bfr) {
+      #pragma unroll
+      for (int i = 0; i < FM; ++i)
+        if (!PARTIAL || i < fmv)
+          #pragma unroll
+          for (int j = 0; j < NF; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    };
+    // Scheduler hint: two MFMAs, then all of the next k-step's fragment reads back to back
+    // (each wave needs many LDS reads in flight to cover LDS latency), then the rest of the
+    // MFMAs.
+    auto interleave = [&]() {
+      if constexpr (!PARTIAL) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, FM + NF, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * NF - 2, 0);
+      }
+    };
+    // k-step kk of the slice in `buf`: multiply set (kk & 1) while reading the next k-step
+    // (of this slice, or k-step 0 of the slice in `nbuf`) into the other set.
+    auto step = [&](int kk, int buf, int nbuf) {
+      const int nb = (kk + 1 < KK) ? buf : nbuf;
+      const int nk = (kk + 1 < KK) ? kk + 1 : 0;
+      if (kk & 1) { read_frags(a0, b0, nb, nk); mfmas(a1, b1); }
+      else        { read_frags(a1, b1, nb, nk); mfmas(a0, b0); }
+      interleave();
+    };
 
-  // ---- main loop -----------------------------------------------------------------------------
-  // Ring of NS stages.  After the fragments of a slice's last k-step are read, one barrier
-  // (a) publishes slice kt+1 (every wave waited for its own copies of it) and (b) frees the
-  // stage of slice kt, which is refilled at once with slice kt+NS; the last k-step's MFMAs
-  // then overlap the reads of slice kt+1's first fragments.  NS-1 slices stay in flight.
-  #pragma unroll
-  for (int s = 0; s < NS; ++s) issue(s, min(s, KT - 1));
-  wait_vmcnt<(NS - 1) * NQW>();
-  __syncthreads();
-  read_frags(a0, b0, 0, 0);
-  int buf = 0;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int nbuf = (buf + 1 == NS) ? 0 : buf + 1;
+    // Ring of NS stages.  After the fragments of a slice's last k-step are read, one barrier
+    // (a) publishes slice kt+1 (every wave waited for its own copies of it) and (b) frees the
+    // stage of slice kt, which is refilled at once with slice kt+NS; the last k-step's MFMAs
+    // then overlap the reads of slice kt+1's first fragments.  NS-1 slices stay in flight.
     #pragma unroll
-    for (int kk = 0; kk < KK - 1; ++kk) step(kk, buf, nbuf);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // all reads of stage buf done
-    wait_vmcnt<(NS - 2) * NQW>();                          // this wave's slice kt+1 landed
+    for (int s = 0; s < NS; ++s) issue(s, min(s, KT - 1));
+    wait_vmcnt<(NS - 1) * NQW>();
     __syncthreads();
-    // past the last slice repeat slice KT-1 (in bounds, never read) so every iteration
-    // leaves the same number of copies outstanding
-    issue(buf, min(kt + NS, KT - 1));
-    step(KK - 1, buf, nbuf);              // after the last slice the reads are stale, unused
-    buf = nbuf;
-  }
-  wait_vmcnt<0>();
+    read_frags(a0, b0, 0, 0);
+    int buf = 0;
+    for (int kt = 0; kt < KT; ++kt) {
+      const int nbuf = (buf + 1 == NS) ? 0 : buf + 1;
+      #pragma unroll
+      for (int kk = 0; kk < KK - 1; ++kk) step(kk, buf, nbuf);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // all reads of stage buf done
+      wait_vmcnt<(NS - 2) * NQW>();                          // this wave's slice kt+1 landed
+      __syncthreads();
+      // past the last slice repeat slice KT-1 (in bounds, never read) so every iteration
+      // leaves the same number of copies outstanding
+      issue(buf, min(kt + NS, KT - 1));
+      step(KK - 1, buf, nbuf);              // after the last slice the reads are stale, unused
+      buf = nbuf;
+    }
+    wait_vmcnt<0>();
+  };
+  if (fmv == FM) main_loop(std::false_type{});
+  else           main_loop(std::true_type{});
 
   // ---- epilogue (as in gemm_kernel) ---------------------------------------------------------
   const int ocol = lane & 31;
