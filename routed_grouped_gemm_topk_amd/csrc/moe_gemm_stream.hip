@@ -74,8 +74,9 @@ __global__ __launch_bounds__(WN * WM * kWave) void stream_kernel(Args g) {
   static_assert((BM + BROWS) % 8 == 0 && WTN % 16 == 0, "whole copies and MFMA tiles");
   static_assert(FM % WM == 0, "fragments split evenly over the wave rows");
   static_assert(NS >= 2 && (NS - 1) * OPS <= 63, "vmcnt range");
-  static_assert(!SCALED || (KK == 1 && BNA == kGroup && BM <= NW * 64),
-                "e4m3: one scale block per slice, one act group per tile");
+  static_assert(!SCALED || (KK == 1 && (UP ? BNA == kGroup : BNA % kGroup == 0) &&
+                            kGroup % WTN == 0 && BM <= NW * 64),
+                "e4m3: one scale block per slice and wave, one act group per up tile");
   static_assert(Op::LB == 16 || Op::LB == 32, "16x16 fragments of one or two 16-byte chunks");
 
   __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
@@ -200,18 +201,18 @@ __global__ __launch_bounds__(WN * WM * kWave) void stream_kernel(Args g) {
     // e4m3: a slice is one k-step and one scale block.  Slices kt+1..kt+NS-2 stay in flight
     // while slice kt is multiplied straight out of its stage; the barrier at the top of each
     // slice both publishes slice kt and retires the stage of slice kt-1 for refilling.
-    // The weight-block scales of this tile (gate and up rows: one row of K/128 each) go to LDS
-    // before the ring starts: a compiler-tracked global load inside the loop would wait on
-    // the untracked ring copies too, draining the ring every slice.
-    __shared__ float sws[2][kMaxDim / kGroup];
+    // The weight-block scales of this tile go to LDS before the ring starts (a compiler-
+    // tracked global load inside the loop would wait on the untracked ring copies too,
+    // draining the ring every slice): up, the gate and the up row-block (one row of K/128
+    // each); down, the BNA/128 row-blocks of the n-block.
+    constexpr int NSW = UP ? 2 : BNA / kGroup;
+    __shared__ float sws[NSW][kMaxDim / kGroup];
     {
       const int wrows = UP ? 2 * g.n_out : g.n_out;
       const float* se = g.w_scales + (size_t)e * (wrows / kGroup) * KB;
-      const float* sw_gate = se + (size_t)(n0 / kGroup) * KB;
-      const float* sw_up = UP ? se + (size_t)((g.n_out + n0) / kGroup) * KB : sw_gate;
-      for (int i = tid; i < KB; i += NT) {
-        sws[0][i] = sw_gate[i];
-        sws[1][i] = sw_up[i];
+      for (int b = 0; b < NSW; ++b) {
+        const int rb = UP ? (b == 0 ? n0 : g.n_out + n0) / kGroup : n0 / kGroup + b;
+        for (int i = tid; i < KB; i += NT) sws[b][i] = se[(size_t)rb * KB + i];
       }
     }
     // An m-block holds its expert's rows first and padding after, so 16-row fragments from
@@ -233,7 +234,9 @@ __global__ __launch_bounds__(WN * WM * kWave) void stream_kernel(Args g) {
       issue(buf == 0 ? NS - 1 : buf - 1, min(kt + NS - 1, KT - 1));   // past the end: repeat, never read
       const char* stg = lds + buf * STAGE;
       const float* sc = reinterpret_cast<const float*>(stg + SC_OFF);
-      const float sw_g = sws[0][kt], sw_u = sws[1][kt];
+      // up: gate / up block scales; down: the block of this wave's columns
+      const float sw_g = UP ? sws[0][kt] : sws[(wn * WTN) / kGroup][kt];
+      const float sw_u = UP ? sws[NSW - 1][kt] : sw_g;
       frag bf[NF];
       #pragma unroll
       for (int j = 0; j < NF; ++j) bf[j] = load_frag(stg + b_row[j], 0);
@@ -465,6 +468,12 @@ hipError_t launch_down_stream(const Resolved& r, const void* act, const float* a
   a.n_slots = (int)r.N;
   a.tiles_max = (int)r.tiles_max;
   a.w_expert_elems = (int64_t)r.H * r.I;
+  if (r.w_dtype == MOE_E4M3 && r.H % 256 == 0 && r.BM >= 64) {
+    // 256-wide n-blocks: twice the weight bytes per slice next to the same gathered rows, so
+    // more of the ring holds weights in flight
+    if (r.BM == 64) return st::run<OpE4M3, 64, 256, 3, false, OUT_BF16, 2>(a, s);
+    return st::run<OpE4M3, 128, 256, 3, false, OUT_BF16, 2>(a, s);
+  }
   if (r.w_dtype == MOE_E4M3) {
     switch (r.BM) {
       case 16: return st::run<OpE4M3, 16, 128, 4, false, OUT_BF16>(a, s);
