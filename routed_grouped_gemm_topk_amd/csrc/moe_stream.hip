@@ -6,38 +6,53 @@ namespace moe {
 
 // ---------------------------------------------------------------------------------------------
 // X quantisation ("MOE Bmm1 Fused Gather", pack_e4m3x2: round to nearest even with
-// saturation to the largest finite e4m3 value).  One wavefront per 128-column group:
-// each lane owns two adjacent bf16 values, the group amax is a wavefront max
+// saturation to the largest finite e4m3 value).  16 lanes per 128-column group, 8 bf16
+// values (16 bytes) per lane, 4 groups per wavefront: the group amax is a 16-lane max
 // reduction, s = amax/448 (IEEE division), codes = e4m3(x/s) (IEEE division).
 // ---------------------------------------------------------------------------------------------
 constexpr int kQuantThreads = 256;
+constexpr int kQuantLanes = kGroup / 8;                            // lanes per group
+constexpr int kQuantGroupsPerBlock = kQuantThreads / kQuantLanes;  // 16
 
 __global__ __launch_bounds__(kQuantThreads) void quant_rows_e4m3_kernel(
-    const uint32_t* __restrict__ x_pairs, uint16_t* __restrict__ xq_pairs,
-    float* __restrict__ scales, int64_t n_groups) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t grp = (int64_t)blockIdx.x * (kQuantThreads / kWave) + threadIdx.x / kWave;
-  if (grp >= n_groups) return;
-  const uint32_t v = x_pairs[grp * (kGroup / 2) + lane];
-  const float a = bf16_bits_to_f32(v & 0xFFFFu);
-  const float b = bf16_bits_to_f32(v >> 16);
-  float m = fmaxf(fabsf(a), fabsf(b));
+    const i32x4* __restrict__ x8, uint2* __restrict__ xq8, float* __restrict__ scales,
+    int64_t n_groups) {
+  const int sub = threadIdx.x & (kQuantLanes - 1);
+  const int64_t grp = (int64_t)blockIdx.x * kQuantGroupsPerBlock + threadIdx.x / kQuantLanes;
+  const bool live = grp < n_groups;
+  float v[8];
+  float m = 0.0f;
+  if (live) {
+    const i32x4 w = x8[grp * kQuantLanes + sub];
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_bits_to_f32((uint32_t)w[i] & 0xFFFFu);
+      v[2 * i + 1] = bf16_bits_to_f32((uint32_t)w[i] >> 16);
+    }
+    #pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+  // the 16 lanes of a group are aligned within the wavefront: xor offsets below 16 stay in it
   #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
+  for (int d = kQuantLanes / 2; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
+  if (!live) return;
   const float s = (m == 0.0f) ? 1.0f : m / kE4M3Max;
-  const uint32_t qa = f32_to_e4m3(a / s);
-  const uint32_t qb = f32_to_e4m3(b / s);
-  xq_pairs[grp * (kGroup / 2) + lane] = (uint16_t)(qa | (qb << 8));
-  if (lane == 0) scales[grp] = s;
+  uint32_t lo = 0, hi = 0;
+  #pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo |= f32_to_e4m3(v[i] / s) << (8 * i);
+    hi |= f32_to_e4m3(v[4 + i] / s) << (8 * i);
+  }
+  xq8[grp * kQuantLanes + sub] = make_uint2(lo, hi);
+  if (sub == 0) scales[grp] = s;
 }
 
 hipError_t launch_quant_rows(const Resolved& r, const void* x, uint8_t* xq, float* scales,
                              hipStream_t s) {
   const int64_t groups = (int64_t)r.T * (r.H / kGroup);
-  const int per_block = kQuantThreads / kWave;
-  const int64_t blocks = (groups + per_block - 1) / per_block;
+  const int64_t blocks = (groups + kQuantGroupsPerBlock - 1) / kQuantGroupsPerBlock;
   hipLaunchKernelGGL(quant_rows_e4m3_kernel, dim3((unsigned)blocks), dim3(kQuantThreads), 0, s,
-                     (const uint32_t*)x, (uint16_t*)xq, scales, groups);
+                     (const i32x4*)x, (uint2*)xq, scales, groups);
   return hipGetLastError();
 }
 
@@ -61,19 +76,31 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   float acc[L];
   #pragma unroll
   for (int i = 0; i < L; ++i) acc[i] = 0.0f;
-  for (int j = 0; j < top_k; ++j) {
-    const int64_t s = (int64_t)t * top_k + j;
-    if (slot_row[s] < 0) continue;
-    const i32x4 v = slot_out[s * vec_per_row + c];
-    if (BF16) {
-      #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += bf16_bits_to_f32((uint32_t)v[i] & 0xFFFFu);
-        acc[2 * i + 1] += bf16_bits_to_f32((uint32_t)v[i] >> 16);
+  // slots in batches of 4: every load of a batch is issued before the first add (a slot
+  // with an excluded id was never written, so its vector is loaded but not added)
+  constexpr int U = 4;
+  for (int j0 = 0; j0 < top_k; j0 += U) {
+    int ok[U];
+    i32x4 v[U];
+    #pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t s = (int64_t)t * top_k + j0 + u;
+      ok[u] = (j0 + u < top_k) ? slot_row[s] >= 0 : 0;
+      v[u] = (j0 + u < top_k) ? slot_out[s * vec_per_row + c] : i32x4{0, 0, 0, 0};
+    }
+    #pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!ok[u]) continue;
+      if (BF16) {
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += bf16_bits_to_f32((uint32_t)v[u][i] & 0xFFFFu);
+          acc[2 * i + 1] += bf16_bits_to_f32((uint32_t)v[u][i] >> 16);
+        }
+      } else {
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += __int_as_float(v[u][i]);
       }
-    } else {
-      #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += __int_as_float(v[i]);
     }
   }
   i32x4 o;
