@@ -122,6 +122,38 @@ def cpu_baseline(case, n_tokens):
                       f"float64 numpy oracle, weights prefetched to host; useful flops 4*n*k*H*I"}
 
 
+def dense_reference(args):
+    """Dense bf16 GEMMs through torch.matmul at the workload's sizes: the whole up projection
+    as one [N, H] x [H, 2I] product, the whole down projection [N, I] x [I, H], and one expert's
+    average share of each.  A comparison point for the grouped kernels, not part of the path."""
+    import torch
+    from moe_inputs import CONFIGS
+    cfg = CONFIGS[args.workload]
+    N = cfg.T * cfg.top_k
+    per = max(1, N // cfg.E)
+    shapes = [("up, whole batch", N, 2 * cfg.I, cfg.H), ("down, whole batch", N, cfg.H, cfg.I),
+              ("up, one expert", per, 2 * cfg.I, cfg.H), ("down, one expert", per, cfg.H, cfg.I)]
+    dev = torch.device("cuda:0")
+    for name, m, n, k in shapes:
+        a = torch.randn(m, k, device=dev, dtype=torch.bfloat16)
+        b = torch.randn(n, k, device=dev, dtype=torch.bfloat16)      # row-major weights [N, K]
+        for _ in range(3):
+            torch.matmul(a, b.t())
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, b.t())
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = 2 * m * n * k / ms / 1e9
+        print(json.dumps({"dense_reference": name, "m": m, "n": n, "k": k, "ms": round(ms, 4),
+                          "TFLOP/s": round(tf, 1), "pct_mfma_peak": round(100 * tf / PEAK_TFLOPS["bf16"], 2)}),
+              flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +164,9 @@ def main():
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (to scale FETCH_SIZE/WRITE_SIZE)")
+    ap.add_argument("--dense-reference", action="store_true",
+                    help="only time torch.matmul (the vendor BLAS) on dense bf16 GEMMs of the "
+                         "workload's sizes: the practical MFMA ceiling of this chip")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this layer runs on one GPU only (no sharding, no collectives); "
@@ -149,6 +184,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
+
+    if args.dense_reference:
+        dense_reference(args)
         return
 
     import routed_grouped_gemm_topk_amd as moe
