@@ -12,6 +12,7 @@ from .configs import CONFIGS, MoEConfig, get_config  # noqa: F401
 from .generate import (  # noqa: F401
     MoECase,
     make_case,
+    make_logits,
     make_routing,
     routing_stats,
     slab_seed,

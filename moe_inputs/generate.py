@@ -50,11 +50,17 @@ def _rng(seed: int, tag: int, e: int = 0) -> np.random.Generator:
     return np.random.default_rng(slab_seed(seed, tag, e))
 
 
-def make_routing(cfg: MoEConfig, seed: int = 0):
-    """Router output on the host: (ids int32 [T,k], w float32 [T,k], probs float64 [T,E])."""
+def make_logits(cfg: MoEConfig, seed: int = 0) -> np.ndarray:
+    """Router logits [T, E] (float64): N(0,1), plus the per-expert bias of the skewed workload."""
     logits = _rng(seed, TAG_LOGITS).standard_normal((cfg.T, cfg.E))
     if cfg.logit_bias_std:
         logits = logits + cfg.logit_bias_std * _rng(seed, TAG_BIAS).standard_normal(cfg.E)[None, :]
+    return logits
+
+
+def make_routing(cfg: MoEConfig, seed: int = 0):
+    """Router output on the host: (ids int32 [T,k], w float32 [T,k], probs float64 [T,E])."""
+    logits = make_logits(cfg, seed)
     z = logits - logits.max(axis=1, keepdims=True)
     p = np.exp(z)
     p /= p.sum(axis=1, keepdims=True)

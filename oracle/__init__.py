@@ -12,7 +12,9 @@ Parity pins: alignment (brute-force sort + worked example), layer (dense
 SwiGLU MLP reduction, mean-of-experts, permutation equivariance, linearity,
 closed-form worked example), e4m3 codec (all 256 codes, ties, saturation,
 torch's float8_e4m3fn), group quantisation (error bound, amax code), bf16
-rounding (torch's bfloat16 cast), combine order (crafted cancellation).  No
+rounding (torch's bfloat16 cast), combine order (crafted cancellation), routing
+(worked examples with ties, brute force over expert subsets, the closed form of a
+renormalised pair).  No
 function here is "parity unpinned".
 """
 from .moe_oracle import (  # noqa: F401
@@ -25,10 +27,12 @@ from .moe_oracle import (  # noqa: F401
     e4m3_decode,
     e4m3_encode,
     expert_down,
+    expert_histogram,
     expert_up,
     max_padded_slots,
     max_tiles,
     moe_layer,
     quantize_groups_e4m3,
+    route,
     silu,
 )

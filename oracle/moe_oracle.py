@@ -137,6 +137,50 @@ def dequantize_blocks(codes, scales, block: int = 128) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------------------------
+# Routing (the step that produces the layer's ids and weights)
+# --------------------------------------------------------------------------------------------
+def route(logits, top_k: int, renormalize: bool):
+    """Router producer: logits [T, E] -> (ids int32 [T, top_k], weights float64 [T, top_k]).
+
+    [topk-softmax] "MOE Bmm1 Fused Gather" (bench setup: topk(logits, experts_per_token,
+    apply_softmax=True), then the expert histogram col_sum) and "factor_moe_fused_gemm.cu"
+    ("factor 0", topk_softmax, which yields topk_weights and topk_ids).  The pages fix neither
+    the order of softmax and selection nor ties; reading: the softmax over all E logits, the
+    top_k experts in descending probability with ties to the lower expert id, their
+    probabilities as weights, renormalised to sum 1 when asked (the same as a softmax over
+    the selected logits).  Softmax is strictly increasing in the logit, so the selection is
+    made on the logits themselves.
+    """
+    lg = np.asarray(logits, dtype=np.float64)
+    T, E = lg.shape
+    if not 1 <= top_k <= E:
+        raise ValueError("need 1 <= top_k <= E")
+    ids = np.empty((T, top_k), dtype=np.int32)
+    w = np.empty((T, top_k), dtype=np.float64)
+    for t in range(T):
+        row = lg[t]
+        # descending logit; among equal logits the lower id first
+        order = sorted(range(E), key=lambda e: (-row[e], e))[:top_k]
+        z = np.exp(row - row.max())
+        p = z / z.sum()
+        sel = np.array([p[e] for e in order])
+        if renormalize:
+            sel = sel / sel.sum()
+        ids[t] = order
+        w[t] = sel
+    return ids, w
+
+
+def expert_histogram(topk_ids, num_experts: int) -> np.ndarray:
+    """Slots routed to each expert ("MOE Bmm1 Fused Gather": col_sum of the top-k mask)."""
+    counts = np.zeros(num_experts, dtype=np.int64)
+    for e in np.asarray(topk_ids).reshape(-1):
+        if 0 <= e < num_experts:
+            counts[e] += 1
+    return counts
+
+
+# --------------------------------------------------------------------------------------------
 # Alignment
 # --------------------------------------------------------------------------------------------
 def max_padded_slots(n_slots: int, num_experts: int, block_m: int) -> int:

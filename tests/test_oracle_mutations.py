@@ -112,3 +112,47 @@ def test_align_mutant_is_caught(mutant, monkeypatch):
     pins = [lambda c=c: ta.test_align_worked_examples(c) for c in cases]
     pins += [lambda: ta.test_align_matches_brute_force(*next(iter(ta.adversarial_routings())))]
     assert _some_pin_fails(pins)
+
+
+# ---- routing -----------------------------------------------------------------------------
+import test_oracle_route as tr  # noqa: E402
+
+_ORIG_ROUTE = mo.route
+
+
+def _route_ties_high(logits, top_k, renormalize):
+    # ties broken toward the higher id
+    lg = np.asarray(logits, np.float64)
+    ids, w = _ORIG_ROUTE(lg[:, ::-1], top_k, renormalize)
+    return (lg.shape[1] - 1 - ids).astype(np.int32), w
+
+
+def _route_ascending(logits, top_k, renormalize):
+    ids, w = _ORIG_ROUTE(-np.asarray(logits, np.float64), top_k, renormalize)
+    lg = np.asarray(logits, np.float64)
+    p = np.exp(lg - lg.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    w = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    if renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    return ids, w
+
+
+def _route_never_renormalises(logits, top_k, renormalize):
+    return _ORIG_ROUTE(logits, top_k, False)
+
+
+def _route_always_renormalises(logits, top_k, renormalize):
+    return _ORIG_ROUTE(logits, top_k, True)
+
+
+ROUTE_PINS = [tr.test_worked_example_ties_no_renorm, tr.test_worked_example_renormalised_subset,
+              tr.test_renormalised_pair_is_a_logistic, tr.test_selection_matches_brute_force,
+              tr.test_weights_are_the_softmax_probabilities]
+
+
+@pytest.mark.parametrize("mutant", [_route_ties_high, _route_ascending, _route_never_renormalises,
+                                    _route_always_renormalises])
+def test_route_mutant_is_caught(mutant, monkeypatch):
+    monkeypatch.setattr(oracle, "route", mutant)
+    assert _some_pin_fails(ROUTE_PINS)
