@@ -162,6 +162,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--block-m", type=int, default=0)
+    ap.add_argument("--routing", choices=["on", "off"], default="off",
+                    help="on: the step starts from router logits (moe_route_align replaces "
+                         "moe_align and produces the ids and weights the GEMMs use)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (to scale FETCH_SIZE/WRITE_SIZE)")
     ap.add_argument("--dense-reference", action="store_true",
@@ -210,7 +213,13 @@ def main():
     slot_out = torch.empty((cfg.T * cfg.top_k, cfg.H), dtype=case.x.dtype, device=dev)
     out = torch.empty((cfg.T, cfg.H), dtype=case.x.dtype, device=dev)
     ws = moe.alloc_workspace(p, dev)
-    stages = ["align"] + (["quant"] if fp8 else []) + ["up", "down", "combine"]
+    routing = args.routing == "on"
+    if routing:
+        from moe_inputs import make_logits
+        logits = torch.from_numpy(make_logits(cfg, 0).astype(np.float32)).to(dev)
+        r_ids = torch.empty((cfg.T, cfg.top_k), dtype=torch.int32, device=dev)
+        r_w = torch.empty((cfg.T, cfg.top_k), dtype=torch.float32, device=dev)
+    stages = ["route_align" if routing else "align"] + (["quant"] if fp8 else []) + ["up", "down", "combine"]
 
     def step(evs=None):
         i = 0
@@ -221,8 +230,13 @@ def main():
                 evs[i].record()
             i += 1
         mark()
-        moe.moe_align(p, case.topk_ids, a["counts"], a["offsets"], a["sorted_slots"], a["slot_row"],
-                      a["tiles"], a["num_tiles"], a["n_invalid"])
+        if routing:
+            moe.moe_route_align(p, logits, cfg.renormalize, r_ids, r_w, a["counts"], a["offsets"],
+                                a["sorted_slots"], a["slot_row"], a["tiles"], a["num_tiles"],
+                                a["n_invalid"])
+        else:
+            moe.moe_align(p, case.topk_ids, a["counts"], a["offsets"], a["sorted_slots"],
+                          a["slot_row"], a["tiles"], a["num_tiles"], a["n_invalid"])
         mark()
         x_in = case.x
         if fp8:
@@ -232,7 +246,8 @@ def main():
         moe.moe_grouped_gemm_up(p, x_in, x_scales, case.w13, case.w13_scales, a["sorted_slots"], a["offsets"],
                                 a["tiles"], a["num_tiles"], act, act_scales)
         mark()
-        moe.moe_grouped_gemm_down(p, act, act_scales, case.w2, case.w2_scales, case.topk_weights,
+        moe.moe_grouped_gemm_down(p, act, act_scales, case.w2, case.w2_scales,
+                                  r_w if routing else case.topk_weights,
                                   a["sorted_slots"], a["offsets"], a["tiles"], a["num_tiles"], slot_out)
         mark()
         moe.moe_combine(p, slot_out, a["slot_row"], out)
@@ -267,7 +282,30 @@ def main():
     torch.cuda.synchronize()
     ms_forward = (time.perf_counter() - t2) * 1e3 / args.steps
 
+    routing_cmp = None
+    if routing:
+        # the same work as two launches (moe_route, then moe_align), for comparison
+        def two_launches():
+            moe.moe_route(p, logits, cfg.renormalize, r_ids, r_w)
+            moe.moe_align(p, r_ids, a["counts"], a["offsets"], a["sorted_slots"], a["slot_row"],
+                          a["tiles"], a["num_tiles"], a["n_invalid"])
+        for _ in range(3):
+            two_launches()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            two_launches()
+        e1.record()
+        torch.cuda.synchronize()
+        routing_cmp = {"route_align_ms": round(kern_ms["route_align"], 5),
+                       "route_then_align_ms": round(e0.elapsed_time(e1) / args.steps, 5)}
+
     work, active = algorithmic_work(cfg, case.ids_host, bm, rows, mt)
+    if routing:
+        w_al = work.pop("align")
+        work = {"route_align": dict(flops=0, bytes=w_al["bytes"] + 4 * cfg.T * cfg.E
+                                    + 8 * cfg.T * cfg.top_k), **work}
     layer_flops_4 = cfg.useful_flops_up
     layer_flops_6 = cfg.useful_flops_layer
     layer_bytes = sum(w["bytes"] for w in work.values())
@@ -337,6 +375,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if routing_cmp:
+        res["routing"] = routing_cmp
     print(json.dumps(res), flush=True)
 
 

@@ -128,6 +128,32 @@ int moe_align(const moe_problem* p, const int32_t* topk_ids, int32_t* counts, in
               int32_t* n_invalid, void* stream);
 
 /*
+ * moe_route -- router producer: top-k experts and weights from router logits.
+ * ("MOE Bmm1 Fused Gather": topk(logits, experts_per_token, apply_softmax=True);
+ *  "factor_moe_fused_gemm.cu": "factor 0", topk_softmax -> topk_weights, topk_ids.)
+ * For every token t: p = softmax(logits[t, :]) over all E experts (fp32); topk_ids[t, :]
+ * are the top_k experts in descending p, ties to the lower expert id (the selection compares
+ * the logits, which softmax keeps in order); topk_weights[t, j] = p of that expert, divided by
+ * the sum of the top_k chosen p when renormalize != 0.
+ * In:  logits       fp32 [T, E], finite.
+ * Out: topk_ids     int32 [T, top_k];  topk_weights fp32 [T, top_k].
+ * Needs top_k <= 64 (MOE_ERR_SHAPE otherwise).  Deterministic.
+ */
+int moe_route(const moe_problem* p, const float* logits, int renormalize, int32_t* topk_ids,
+              float* topk_weights, void* stream);
+
+/*
+ * moe_route_align -- moe_route followed by moe_align on its ids, as one call: the routing
+ * launch (a wavefront per token) and the alignment launches on `stream`, with no host
+ * synchronisation between them.  Arguments and outputs are those of the two calls; results are
+ * identical to calling them in sequence.
+ */
+int moe_route_align(const moe_problem* p, const float* logits, int renormalize,
+                    int32_t* topk_ids, float* topk_weights, int32_t* counts, int32_t* offsets,
+                    int32_t* sorted_slots, int32_t* slot_row, int32_t* tiles, int32_t* num_tiles,
+                    int32_t* n_invalid, void* stream);
+
+/*
  * moe_quantize_rows_e4m3 -- fp8 workload only (dtype BF16, w_dtype E4M3).
  * ("MOE Bmm1 Fused Gather", pack_e4m3x2: round to nearest even, saturate to finite.)
  * For each token row t and 128-column group g of x (bf16 [T,H]):

@@ -37,6 +37,8 @@ from ._lib import (  # noqa: F401
     moe_max_tiles,
     moe_pick_block_m,
     moe_quantize_rows_e4m3,
+    moe_route,
+    moe_route_align,
     moe_validate,
     moe_workspace_bytes,
     status_str,
@@ -56,6 +58,26 @@ def align(p: Problem, topk_ids: torch.Tensor, stream=None) -> dict:
     a = alloc_align(p, topk_ids.device)
     moe_align(p, topk_ids, a["counts"], a["offsets"], a["sorted_slots"], a["slot_row"],
               a["tiles"], a["num_tiles"], a["n_invalid"], stream)
+    return a
+
+
+def route(p: Problem, logits: torch.Tensor, renormalize: bool, stream=None):
+    """Run moe_route into fresh buffers; returns (topk_ids int32 [T,k], topk_weights fp32 [T,k])."""
+    ids = torch.empty((p.T, p.top_k), dtype=torch.int32, device=logits.device)
+    w = torch.empty((p.T, p.top_k), dtype=torch.float32, device=logits.device)
+    moe_route(p, logits, renormalize, ids, w, stream)
+    return ids, w
+
+
+def route_align(p: Problem, logits: torch.Tensor, renormalize: bool, stream=None) -> dict:
+    """Run moe_route_align into fresh buffers; returns align()'s buffers plus topk_ids and
+    topk_weights."""
+    a = alloc_align(p, logits.device)
+    a["topk_ids"] = torch.empty((p.T, p.top_k), dtype=torch.int32, device=logits.device)
+    a["topk_weights"] = torch.empty((p.T, p.top_k), dtype=torch.float32, device=logits.device)
+    moe_route_align(p, logits, renormalize, a["topk_ids"], a["topk_weights"], a["counts"],
+                    a["offsets"], a["sorted_slots"], a["slot_row"], a["tiles"], a["num_tiles"],
+                    a["n_invalid"], stream)
     return a
 
 

@@ -30,8 +30,9 @@ _DT_NAME = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_E4M3}
 _TORCH_DT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_E4M3: torch.float8_e4m3fn}
 
 EXPORTS = ["moe_status_str", "moe_validate", "moe_pick_block_m", "moe_max_padded_slots",
-           "moe_max_tiles", "moe_workspace_bytes", "moe_align", "moe_quantize_rows_e4m3",
-           "moe_grouped_gemm_up", "moe_grouped_gemm_down", "moe_combine", "moe_forward"]
+           "moe_max_tiles", "moe_workspace_bytes", "moe_route", "moe_route_align", "moe_align",
+           "moe_quantize_rows_e4m3", "moe_grouped_gemm_up", "moe_grouped_gemm_down",
+           "moe_combine", "moe_forward"]
 
 
 class MoeError(RuntimeError):
@@ -81,6 +82,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "moe_max_tiles": (ctypes.c_int64, [P]),
         "moe_workspace_bytes": (ctypes.c_int64, [P]),
         "moe_align": (ctypes.c_int, [P] + [vp] * 8 + [vp]),
+        "moe_route": (ctypes.c_int, [P, vp, ctypes.c_int, vp, vp, vp]),
+        "moe_route_align": (ctypes.c_int, [P, vp, ctypes.c_int] + [vp] * 9 + [vp]),
         "moe_quantize_rows_e4m3": (ctypes.c_int, [P, vp, vp, vp, vp]),
         "moe_grouped_gemm_up": (ctypes.c_int, [P] + [vp] * 10 + [vp]),
         "moe_grouped_gemm_down": (ctypes.c_int, [P] + [vp] * 10 + [vp]),
@@ -180,6 +183,28 @@ def moe_align(p: Problem, topk_ids, counts, offsets, sorted_slots, slot_row, til
             _ptr(slot_row, "slot_row", i32, N), _ptr(tiles, "tiles", i32, 2 * mt),
             _ptr(num_tiles, "num_tiles", i32, 1), _ptr(n_invalid, "n_invalid", i32, 1)]
     _checked(load().moe_align(ctypes.byref(p), *args, _stream(stream)), "moe_align")
+
+
+def moe_route(p: Problem, logits, renormalize: bool, topk_ids, topk_weights, stream=None) -> None:
+    N = p.T * p.top_k
+    args = [_ptr(logits, "logits", torch.float32, p.T * p.E), ctypes.c_int(1 if renormalize else 0),
+            _ptr(topk_ids, "topk_ids", torch.int32, N), _ptr(topk_weights, "topk_weights", torch.float32, N)]
+    _checked(load().moe_route(ctypes.byref(p), *args, _stream(stream)), "moe_route")
+
+
+def moe_route_align(p: Problem, logits, renormalize: bool, topk_ids, topk_weights, counts, offsets,
+                    sorted_slots, slot_row, tiles, num_tiles, n_invalid, stream=None) -> None:
+    N = p.T * p.top_k
+    rows = moe_max_padded_slots(p)
+    mt = moe_max_tiles(p)
+    i32 = torch.int32
+    args = [_ptr(logits, "logits", torch.float32, p.T * p.E), ctypes.c_int(1 if renormalize else 0),
+            _ptr(topk_ids, "topk_ids", i32, N), _ptr(topk_weights, "topk_weights", torch.float32, N),
+            _ptr(counts, "counts", i32, p.E), _ptr(offsets, "offsets", i32, p.E + 1),
+            _ptr(sorted_slots, "sorted_slots", i32, rows), _ptr(slot_row, "slot_row", i32, N),
+            _ptr(tiles, "tiles", i32, 2 * mt), _ptr(num_tiles, "num_tiles", i32, 1),
+            _ptr(n_invalid, "n_invalid", i32, 1)]
+    _checked(load().moe_route_align(ctypes.byref(p), *args, _stream(stream)), "moe_route_align")
 
 
 def moe_quantize_rows_e4m3(p: Problem, x, xq, scales, stream=None) -> None:

@@ -207,8 +207,8 @@ __device__ void finish_layout(const int* cnt, int* tb, int* off, int* wsum, int 
 }
 
 // ---- up to kSmallN slots: one workgroup ---------------------------------------------------
-__global__ __launch_bounds__(kAlignThreads) void align_small_kernel(
-    const int32_t* __restrict__ ids, int N, int E, int BM, int rows_max, int tiles_max,
+__device__ __forceinline__ void align_small(
+    const int32_t* ids, int N, int E, int BM, int rows_max, int tiles_max,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_row,
     int32_t* __restrict__ tiles, int32_t* __restrict__ num_tiles,
@@ -240,6 +240,16 @@ __global__ __launch_bounds__(kAlignThreads) void align_small_kernel(
                 num_tiles, sorted_slots);
   for (int i = lane; i < E; i += kWave) hist[wave][i] += off[i];   // this wave's next rows
   place_keys<kSmallBatch>(k, w, E, key_bits, lane, hist[wave], sorted_slots, slot_row);
+}
+
+__global__ __launch_bounds__(kAlignThreads) void align_small_kernel(
+    const int32_t* __restrict__ ids, int N, int E, int BM, int rows_max, int tiles_max,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_row,
+    int32_t* __restrict__ tiles, int32_t* __restrict__ num_tiles,
+    int32_t* __restrict__ n_invalid) {
+  align_small(ids, N, E, BM, rows_max, tiles_max, counts, offsets, sorted_slots, slot_row, tiles,
+              num_tiles, n_invalid);
 }
 
 // ---- more slots: count / scan / place ---------------------------------------------------

@@ -6,6 +6,7 @@
 #include <mutex>
 
 #include "moe_internal.h"
+#include "moe_route.h"
 
 using namespace moe;
 
@@ -152,6 +153,34 @@ int64_t moe_max_tiles(const moe_problem* p) {
 int64_t moe_workspace_bytes(const moe_problem* p) {
   const int v = validate(p);
   return v != MOE_OK ? v : layout(resolve(p)).total;
+}
+
+int moe_route(const moe_problem* p, const float* logits, int renormalize, int32_t* topk_ids,
+              float* topk_weights, void* stream) {
+  int v = validate(p);
+  if (v) return v;
+  if (p->top_k > kRouteMaxK) return MOE_ERR_SHAPE;
+  if (!logits || !topk_ids || !topk_weights) return MOE_ERR_NULL;
+  if ((v = check_device())) return v;
+  const Resolved r = resolve(p);
+  return status_of(launch_route(r, logits, renormalize, topk_ids, topk_weights, (hipStream_t)stream));
+}
+
+int moe_route_align(const moe_problem* p, const float* logits, int renormalize, int32_t* topk_ids,
+                    float* topk_weights, int32_t* counts, int32_t* offsets, int32_t* sorted_slots,
+                    int32_t* slot_row, int32_t* tiles, int32_t* num_tiles, int32_t* n_invalid,
+                    void* stream) {
+  int v = validate(p);
+  if (v) return v;
+  if (p->top_k > kRouteMaxK) return MOE_ERR_SHAPE;
+  if (!logits || !topk_ids || !topk_weights || !counts || !offsets || !sorted_slots ||
+      !slot_row || !tiles || !num_tiles || !n_invalid)
+    return MOE_ERR_NULL;
+  if ((v = check_device())) return v;
+  const Resolved r = resolve(p);
+  return status_of(launch_route_align(r, logits, renormalize, topk_ids, topk_weights, counts,
+                                      offsets, sorted_slots, slot_row, tiles, num_tiles,
+                                      n_invalid, (hipStream_t)stream));
 }
 
 int moe_align(const moe_problem* p, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,

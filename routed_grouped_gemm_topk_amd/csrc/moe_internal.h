@@ -163,6 +163,12 @@ struct Resolved {
   int64_t tiles_max;       // moe_max_tiles
 };
 
+hipError_t launch_route(const Resolved& r, const float* logits, int renorm, int32_t* topk_ids,
+                        float* topk_w, hipStream_t s);
+hipError_t launch_route_align(const Resolved& r, const float* logits, int renorm, int32_t* topk_ids,
+                              float* topk_w, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_slots, int32_t* slot_row, int32_t* tiles,
+                              int32_t* num_tiles, int32_t* n_invalid, hipStream_t s);
 hipError_t launch_align(const Resolved& r, const int32_t* ids, int32_t* counts, int32_t* offsets,
                         int32_t* sorted_slots, int32_t* slot_row, int32_t* tiles,
                         int32_t* num_tiles, int32_t* n_invalid, hipStream_t s);

@@ -116,3 +116,15 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         moe.moe_combine(p, torch.zeros(16 * 2 * 128, dtype=torch.bfloat16),
                         torch.zeros(32, dtype=torch.int32), torch.zeros(16 * 128, dtype=torch.bfloat16))
+
+
+def test_route_entry_points_validate_on_the_host(lib):
+    """moe_route / moe_route_align: shape errors, the top_k <= 64 limit, then NULL pointers."""
+    p = bad(H=100)
+    assert lib.moe_route(ctypes.byref(p), None, 0, None, None, None) == moe.MOE_ERR_SHAPE
+    assert lib.moe_route_align(ctypes.byref(p), None, 0, *([None] * 10)) == moe.MOE_ERR_SHAPE
+    p = moe.make_problem(4, 128, 128, 100, 65, "bf16")          # top_k above 64
+    assert lib.moe_route(ctypes.byref(p), None, 0, None, None, None) == moe.MOE_ERR_SHAPE
+    p = bad()
+    assert lib.moe_route(ctypes.byref(p), None, 0, None, None, None) == moe.MOE_ERR_NULL
+    assert lib.moe_route_align(ctypes.byref(p), None, 1, *([None] * 10)) == moe.MOE_ERR_NULL

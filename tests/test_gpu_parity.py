@@ -100,6 +100,69 @@ def test_align_adversarial_bit_exact(device, name, ids, E, bm):
     check_alignment(p, torch.from_numpy(ids).to(device), ids)
 
 
+# ---------------------------------------------------------------------------------------------
+# routing (logits -> top-k ids and weights): ids bit-exact (the selection compares the same fp32
+# logits on both sides), weights to fp32 rounding of the softmax
+# ---------------------------------------------------------------------------------------------
+ROUTE_W_RTOL = 1e-5
+
+
+def check_route(ids, w, logits32, k, renorm):
+    o_ids, o_w = oracle.route(logits32.astype(np.float64), k, renorm)
+    assert np.array_equal(to_np(ids), o_ids)
+    assert np.allclose(to_np(w), o_w, rtol=ROUTE_W_RTOL, atol=1e-30)
+    return o_ids
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_route_workloads(device, name):
+    cfg = CONFIGS[name]
+    from moe_inputs import make_logits
+    lg = make_logits(cfg, 0).astype(np.float32)
+    p = problem_of(cfg)
+    say(f"route {name}")
+    ids, w = moe.route(p, torch.from_numpy(lg).to(device), cfg.renormalize)
+    torch.cuda.synchronize()
+    check_route(ids, w, lg, cfg.top_k, cfg.renormalize)
+
+
+def route_cases():
+    rng = np.random.default_rng(21)
+    yield "ties", rng.integers(-2, 3, (300, 16)).astype(np.float32), 4
+    yield "E1", rng.standard_normal((50, 1)).astype(np.float32), 1
+    yield "k_equals_E", rng.standard_normal((40, 8)).astype(np.float32), 8
+    yield "E1024_k8", rng.standard_normal((70, 1024)).astype(np.float32) * 4, 8
+    yield "E65_k64", rng.standard_normal((9, 65)).astype(np.float32), 64
+    yield "E200_k6_ties", np.repeat(rng.integers(0, 3, (33, 25)).astype(np.float32), 8, axis=1), 6
+    yield "T1", rng.standard_normal((1, 256)).astype(np.float32), 8
+    yield "T128", rng.standard_normal((128, 256)).astype(np.float32), 8
+    yield "T129", rng.standard_normal((129, 256)).astype(np.float32), 8
+    yield "large_T", rng.standard_normal((5000, 64)).astype(np.float32) * 2, 6
+    yield "E1024_T32", rng.standard_normal((32, 1024)).astype(np.float32), 8
+    yield "E512_T64_k16", rng.standard_normal((64, 512)).astype(np.float32), 16
+
+
+@pytest.mark.parametrize("name,lg,k", list(route_cases()), ids=lambda v: v if isinstance(v, str) else "")
+@pytest.mark.parametrize("renorm", [False, True])
+def test_route_and_route_align(device, name, lg, k, renorm):
+    T, E = lg.shape
+    p = moe.make_problem(T, 128, 128, E, k, "bf16")
+    d = torch.from_numpy(lg).to(device)
+    say(f"route {name} renorm={renorm}")
+    ids, w = moe.route(p, d, renorm)
+    a = moe.route_align(p, d, renorm)
+    torch.cuda.synchronize()
+    o_ids = check_route(ids, w, lg, k, renorm)
+    assert torch.equal(a["topk_ids"], ids) and torch.equal(a["topk_weights"], w)
+    o = oracle.align(o_ids, E, moe.moe_pick_block_m(p))
+    assert to_np(a["counts"]).tolist() == o.counts.tolist()
+    assert to_np(a["offsets"]).tolist() == o.offsets.tolist()
+    assert np.array_equal(to_np(a["sorted_slots"]), o.sorted_slots)
+    assert np.array_equal(to_np(a["slot_row"]), o.slot_row)
+    assert np.array_equal(to_np(a["tiles"]).reshape(-1, 2), o.tiles)
+    assert int(a["num_tiles"].item()) == o.num_tiles and int(a["n_invalid"].item()) == 0
+
+
 def test_align_deterministic_across_streams(device):
     cfg = CONFIGS["skewed_prefill_bf16"]
     from moe_inputs import make_routing
