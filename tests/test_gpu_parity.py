@@ -441,3 +441,41 @@ def test_forward_full_size_sampled(device, name):
     assert err <= tol_of(cfg)
     del case
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------------------------
+# maximum dimensions: the largest K (H = 32768, the whole zero row) and an expert weight slab
+# just under 2^31 bytes (the limit of the kernels' 32-bit in-slab offsets), through every GEMM
+# family: streaming (block_m 64), prefill (128, 256) and e4m3
+# ---------------------------------------------------------------------------------------------
+MAX_DIMS = {
+    "bf16_bm64": ("mixtral_prefill_bf16", dict(T=24, H=32768, I=16256, E=2, top_k=2), 64),
+    "bf16_bm128": ("mixtral_prefill_bf16", dict(T=24, H=32768, I=16256, E=2, top_k=2), 128),
+    "bf16_bm256": ("mixtral_prefill_bf16", dict(T=24, H=32768, I=16256, E=2, top_k=2), 256),
+    "e4m3_bm128": ("dsv3_fp8_e4m3", dict(T=24, H=32768, I=32640, E=2, top_k=2), 128),
+}
+
+
+@pytest.mark.parametrize("label", list(MAX_DIMS))
+def test_forward_full_size_max_dims(device, label):
+    base, kw, bm = MAX_DIMS[label]
+    cfg = get_config(base, **kw)
+    p = problem_of(cfg, bm)
+    assert moe.moe_validate(p) == moe.MOE_OK
+    say(f"max dims {label}: generating")
+    case = make_case(cfg, device, seed=3)
+    torch.cuda.synchronize()
+    say(f"max dims {label}: running")
+    check_alignment(p, case.topk_ids, case.ids_host)
+    out, _ = run_forward(case, bm)
+    torch.cuda.synchronize()
+    say(f"max dims {label}: oracle")
+    ref = oracle.moe_layer(case.x_host(), case.ids_host, case.w_host,
+                           expert_getter(case, cache=False), cfg.E, fp8=cfg.w_dtype == "e4m3")
+    got = to_np(out.to(torch.float32))
+    err = rel_err(got, ref)
+    say(f"  rel err {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= tol_of(cfg)
+    del case
+    torch.cuda.empty_cache()
