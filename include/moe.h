@@ -62,7 +62,8 @@ typedef enum moe_dtype {
  *                              scale per 128x128 block (dequantised W = code*scale);
  *                              X and act quantised to e4m3 per (row, 128-column
  *                              group) with scale amax/448; bf16 slot rows.
- * Limits: 1 <= top_k <= E <= 1024; T >= 1; H and I multiples of 128, at most 32768;
+ * Limits: 1 <= top_k <= E <= 1024; T >= 1; H and I multiples of 64 (of 128 with E4M3
+ *         weights), at most 32768;
  *         T*top_k < 2^31 and per-expert weight slabs < 2^31 bytes.
  * block_m: rows per m-block of the expert-sorted slot list, one of 16, 32, 64,
  *          128, or 256 (bf16 problems only); 0 lets the library choose

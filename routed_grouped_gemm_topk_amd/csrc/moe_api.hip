@@ -36,7 +36,10 @@ int32_t choose_block_m(const moe_problem* p) {
 int validate(const moe_problem* p) {
   if (!p) return MOE_ERR_NULL;
   if (p->T < 1 || p->E < 1 || p->E > 1024 || p->top_k < 1 || p->top_k > p->E) return MOE_ERR_SHAPE;
-  if (p->H < 128 || p->I < 128 || p->H % 128 || p->I % 128) return MOE_ERR_SHAPE;
+  // H and I: multiples of 64 (whole 64-wide k-slices and n-blocks); e4m3 needs 128 (one
+  // scale block per 128 values)
+  if (p->H < 64 || p->I < 64 || p->H % 64 || p->I % 64) return MOE_ERR_SHAPE;
+  if (p->w_dtype == MOE_E4M3 && (p->H % 128 || p->I % 128)) return MOE_ERR_SHAPE;
   if (p->H > kMaxDim || p->I > kMaxDim) return MOE_ERR_SHAPE;
   if (p->block_m != 0 && p->block_m != 16 && p->block_m != 32 && p->block_m != 64 &&
       p->block_m != 128 && p->block_m != 256)

@@ -355,6 +355,18 @@ static hipError_t run(const GemmArgs& a, int n_blocks_n, hipStream_t s) {
 // 128).  Waves: 2x2 for 128-row blocks, 1x4 for smaller blocks (all waves along N).
 template <class Op, int BK, bool UP, int OUT>
 static hipError_t dispatch_bm(const Resolved& r, const GemmArgs& a, hipStream_t s) {
+  if constexpr (!std::is_same<Op, OpE4M3>::value) {
+    if (a.n_out % 128 != 0) {   // n_out a multiple of 64 only (bf16 / fp32): 64-wide n-blocks
+      const int nb = a.n_out / 64;
+      switch (r.BM) {
+        case 16: return run<Op, 16, 64, BK, 1, 4, UP, OUT>(a, nb, s);
+        case 32: return run<Op, 32, 64, BK, 1, 4, UP, OUT>(a, nb, s);
+        case 64: return run<Op, 64, 64, BK, 1, 4, UP, OUT>(a, nb, s);
+        case 128: return run<Op, 128, 64, BK, 2, 2, UP, OUT>(a, nb, s);
+        default: return hipErrorInvalidValue;
+      }
+    }
+  }
   const int nb = a.n_out / 128;
   switch (r.BM) {
     case 16: return run<Op, 16, 128, BK, 1, 4, UP, OUT>(a, nb, s);

@@ -557,6 +557,10 @@ hipError_t launch_up_prefill(const Resolved& r, const void* x, const void* w13,
   a.tiles_max = (int)r.tiles_max;
   a.w_expert_elems = (int64_t)2 * r.I * r.H;
   // 256-row m-blocks: 8 waves, 4 along M (64 rows each) x 2 along N
+  if (r.I % 128 != 0) {   // I a multiple of 64 only: 64-wide n-blocks, 2 waves along N
+    if (r.BM == 256) return pf::run_dma<64, 3, 64, true, 4, 256, 2>(a, s);
+    return pf::run_dma<64, 4, 64, true, 4, 128, 2>(a, s);
+  }
   if (r.BM == 256) return pf::run_dma<64, 2, 128, true, 4, 256, 2>(a, s);
   if (r.I % 256 == 0) return pf::run_dma<64, 2, 256, true, 2>(a, s);
   return pf::run_dma<64, 3, 128, true>(a, s);
@@ -581,6 +585,10 @@ hipError_t launch_down_prefill(const Resolved& r, const void* act, const void* w
   a.n_slots = (int)r.N;
   a.tiles_max = (int)r.tiles_max;
   a.w_expert_elems = (int64_t)r.H * r.I;
+  if (r.H % 128 != 0) {   // H a multiple of 64 only
+    if (r.BM == 256) return pf::run_dma<64, 3, 64, false, 4, 256, 2>(a, s);
+    return pf::run_dma<64, 4, 64, false, 4, 128, 2>(a, s);
+  }
   if (r.BM == 256) {
     if (r.H % 256 == 0) return pf::run_dma<64, 2, 256, false, 4, 256, 2>(a, s);
     return pf::run_dma<64, 2, 128, false, 4, 256, 2>(a, s);

@@ -441,6 +441,13 @@ hipError_t launch_up_stream(const Resolved& r, const void* x, const float* x_sca
       default: return st::run<OpE4M3, 128, 128, 3, true, OUT_E4M3, 2>(a, s);
     }
   }
+  if (r.I % 128 != 0) {   // I a multiple of 64 only: 64-wide n-blocks
+    switch (r.BM) {
+      case 16: return st::run<OpBf16, 16, 64, 6, true, OUT_BF16>(a, s);
+      case 32: return st::run<OpBf16, 32, 64, 6, true, OUT_BF16>(a, s);
+      default: return st::run<OpBf16, 64, 64, 5, true, OUT_BF16>(a, s);
+    }
+  }
   switch (r.BM) {
     case 16: return st::run<OpBf16, 16, 128, 4, true, OUT_BF16>(a, s);
     case 32: return st::run<OpBf16, 32, 128, 4, true, OUT_BF16>(a, s);
@@ -487,6 +494,13 @@ hipError_t launch_down_stream(const Resolved& r, const void* act, const float* a
       case 16: return st::run<OpBf16, 16, 256, 4, false, OUT_BF16>(a, s);
       case 32: return st::run<OpBf16, 32, 256, 4, false, OUT_BF16>(a, s);
       default: return st::run<OpBf16, 64, 256, 3, false, OUT_BF16>(a, s);
+    }
+  }
+  if (r.H % 128 != 0) {   // H a multiple of 64 only: 64-wide n-blocks
+    switch (r.BM) {
+      case 16: return st::run<OpBf16, 16, 64, 8, false, OUT_BF16>(a, s);
+      case 32: return st::run<OpBf16, 32, 64, 8, false, OUT_BF16>(a, s);
+      default: return st::run<OpBf16, 64, 64, 6, false, OUT_BF16>(a, s);
     }
   }
   switch (r.BM) {   // H is a multiple of 128 only

@@ -46,7 +46,8 @@ def bad(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(T=0), moe.MOE_ERR_SHAPE), (dict(H=100), moe.MOE_ERR_SHAPE), (dict(I=192), moe.MOE_ERR_SHAPE),
+    (dict(T=0), moe.MOE_ERR_SHAPE), (dict(H=100), moe.MOE_ERR_SHAPE), (dict(I=160), moe.MOE_ERR_SHAPE),
+    (dict(I=192, w_dtype="e4m3"), moe.MOE_ERR_SHAPE), (dict(H=64, w_dtype="e4m3"), moe.MOE_ERR_SHAPE),
     (dict(E=0), moe.MOE_ERR_SHAPE), (dict(E=1025, top_k=2), moe.MOE_ERR_SHAPE),
     (dict(top_k=0), moe.MOE_ERR_SHAPE), (dict(top_k=9), moe.MOE_ERR_SHAPE),
     (dict(block_m=48), moe.MOE_ERR_SHAPE), (dict(block_m=512), moe.MOE_ERR_SHAPE),
@@ -60,6 +61,12 @@ def test_validation_codes(kw, code):
     assert moe.moe_validate(bad(**kw)) == code
     with pytest.raises(moe.MoeError):
         moe.moe_workspace_bytes(bad(**kw))
+
+
+def test_multiples_of_64_are_valid_for_bf16_and_fp32():
+    for dt in ("bf16", "f32"):
+        assert moe.moe_validate(bad(H=192, I=2880, dtype=dt, w_dtype=dt)) == moe.MOE_OK
+        assert moe.moe_validate(bad(H=64, I=64, dtype=dt, w_dtype=dt)) == moe.MOE_OK
 
 
 def test_null_problem(lib):

@@ -236,6 +236,9 @@ SMALL = {
     # H an odd multiple of 128: the widest n-blocks do not divide it
     "dsv3_decode_bf16@h384": dict(T=48, H=384, I=384),
     "dsv3_fp8_e4m3@h384": dict(T=120, H=384, I=384, E=16),
+    # H and I odd multiples of 64 (64-wide n-blocks; GPT-OSS has H = I = 2880)
+    "mixtral_prefill_bf16@h64": dict(T=300, H=192, I=320),
+    "tiny_fp32@h64": dict(H=192, I=320),
 }
 
 _cases = {}
