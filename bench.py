@@ -154,6 +154,126 @@ def dense_reference(args):
               flush=True)
 
 
+def sweep(args):
+    """The 48-point batch sweep of one expert-parallel shard ("MOE Bmm1 Fused Gather", its bench:
+    batch sizes and production-like routing).  Per batch size: the whole layer (align, up, down,
+    combine) at the library's block_m, and optionally at each block_m of --sweep-block-m; one JSON
+    line per point with the up kernel's and the layer's times, useful TFLOP/s (local slots only)
+    and the up kernel's roofline fraction max(flops/peak, bytes/HBM peak) / time."""
+    import numpy as np
+    import torch
+
+    import routed_grouped_gemm_topk_amd as moe
+    from moe_inputs import (SWEEP_CONFIGS, get_config, make_case, make_routing, make_x,
+                            sweep_batch_sizes)
+
+    base = SWEEP_CONFIGS[args.sweep]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"generating {base.name} weights and X[{base.T}, {base.H}] on {torch.cuda.get_device_name(dev)}")
+    case = make_case(get_config(base.name, T=base.top_k), dev, seed=0)   # weights (X regenerated below)
+    x_all = torch.from_numpy(make_x(base, 0)).to(torch.bfloat16).to(dev)
+    batches = sweep_batch_sizes(base.route_experts or base.E, base.top_k)
+    if args.sweep_points:
+        batches = [batches[int(i)] for i in args.sweep_points.split(",")]
+    cands = [int(v) for v in args.sweep_block_m.split(",")] if args.sweep_block_m else []
+    peak_tf = PEAK_TFLOPS[base.w_dtype]
+    E, H, I, K = base.E, base.H, base.I, base.top_k
+    rows_md = []
+    for T in batches:
+        cfg = get_config(base.name, T=T)
+        ids_h, w_h, _ = make_routing(cfg, 0)
+        ids = torch.from_numpy(ids_h).to(dev)
+        wts = torch.from_numpy(w_h).to(dev)
+        x = x_all[:T]
+        counts = np.bincount(ids_h.reshape(-1), minlength=E)[:E]
+        n_loc = int(counts.sum())
+        active = int((counts > 0).sum())
+        up_flops = 4 * n_loc * H * I
+        up_bytes = n_loc * H * 2 + active * 2 * I * H * 2 + n_loc * I * 2
+        roof_ms = max(up_flops / (peak_tf * 1e12), up_bytes / (PEAK_HBM_GBS * 1e9)) * 1e3
+
+        def run(bm):
+            p = moe.make_problem(T, H, I, E, K, "bf16", base.w_dtype, bm)
+            bm_used = moe.moe_pick_block_m(p)
+            a = moe.alloc_align(p, dev)
+            act = torch.empty((moe.moe_max_padded_slots(p), I), dtype=torch.bfloat16, device=dev)
+            slot_out = torch.empty((T * K, H), dtype=torch.bfloat16, device=dev)
+            out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+            def step(ev=None):
+                if ev: ev[0].record()
+                moe.moe_align(p, ids, a["counts"], a["offsets"], a["sorted_slots"], a["slot_row"],
+                              a["tiles"], a["num_tiles"], a["n_invalid"])
+                if ev: ev[1].record()
+                moe.moe_grouped_gemm_up(p, x, None, case.w13, None, a["sorted_slots"], a["offsets"],
+                                        a["tiles"], a["num_tiles"], act, None)
+                if ev: ev[2].record()
+                moe.moe_grouped_gemm_down(p, act, None, case.w2, None, wts, a["sorted_slots"],
+                                          a["offsets"], a["tiles"], a["num_tiles"], slot_out)
+                if ev: ev[3].record()
+                moe.moe_combine(p, slot_out, a["slot_row"], out)
+                if ev: ev[4].record()
+            for _ in range(args.warmup):
+                step()
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            for k in range(args.steps):
+                step(evs[k])
+            torch.cuda.synchronize()
+            st = lambda i, j: float(np.mean([e[i].elapsed_time(e[j]) for e in evs]))  # noqa: E731
+            n_inv = int(a["n_invalid"].item())
+            if n_inv != T * K - n_loc:
+                raise RuntimeError(f"T={T}: n_invalid {n_inv} != {T * K - n_loc}")
+            return bm_used, {"align": st(0, 1), "up": st(1, 2), "down": st(2, 3),
+                             "combine": st(3, 4), "layer": st(0, 4)}
+
+        bm0, t0 = run(args.block_m)
+        best = None
+        for bm in cands:
+            if bm == 256 and base.w_dtype != "bf16":
+                continue
+            _, t = run(bm)
+            if best is None or t["layer"] < best[1]["layer"]:
+                best = (bm, t)
+        pt = {"sweep": base.name, "T": T, "tokens_per_expert": T * K // (base.route_experts or E),
+              "local_slots": n_loc, "active_experts": active, "max_per_expert": int(counts.max()),
+              "block_m": bm0, **{f"{k}_ms": round(v, 5) for k, v in t0.items()},
+              "up_TFLOP/s": round(up_flops / t0["up"] / 1e9, 1),
+              "up_pct_mfma_peak": round(100 * up_flops / t0["up"] / 1e9 / peak_tf, 2),
+              "up_GB/s": round(up_bytes / t0["up"] / 1e6, 1),
+              "up_roofline_frac": round(roof_ms / t0["up"], 4),
+              "layer_TFLOP/s": round(1.5 * up_flops / t0["layer"] / 1e9, 1)}
+        if best:
+            pt["best_block_m"] = best[0]
+            pt["best_layer_ms"] = round(best[1]["layer"], 5)
+            pt["best_up_ms"] = round(best[1]["up"], 5)
+        print(json.dumps(pt), flush=True)
+        rows_md.append(pt)
+        del ids, wts
+        torch.cuda.empty_cache()
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            f.write(f"# Batch sweep: {base.name}\n\n{base.description}.\n\n")
+            f.write("Command: `python bench.py " + " ".join(sys.argv[1:]) + "`\n\n")
+            f.write(f"Device: {torch.cuda.get_device_name(dev)}; kernel_source_sha256 "
+                    f"`{kernel_source_digest()}`; times are HIP-event means over {args.steps} steps "
+                    f"after {args.warmup} warmup steps.\n\n")
+            hdr = ["T", "tok/exp", "local slots", "max/exp", "bm", "up ms", "up TF/s", "up % peak",
+                   "up roofline frac", "layer ms", "layer TF/s"]
+            if cands:
+                hdr += ["best bm", "best layer ms"]
+            f.write("| " + " | ".join(hdr) + " |\n|" + "---|" * len(hdr) + "\n")
+            for r in rows_md:
+                v = [r["T"], r["tokens_per_expert"], r["local_slots"], r["max_per_expert"], r["block_m"],
+                     r["up_ms"], r["up_TFLOP/s"], r["up_pct_mfma_peak"], r["up_roofline_frac"],
+                     r["layer_ms"], r["layer_TFLOP/s"]]
+                if cands:
+                    v += [r.get("best_block_m"), r.get("best_layer_ms")]
+                f.write("| " + " | ".join(str(c) for c in v) + " |\n")
+        log(f"wrote {args.sweep_out}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +290,14 @@ def main():
     ap.add_argument("--dense-reference", action="store_true",
                     help="only time torch.matmul (the vendor BLAS) on dense bf16 GEMMs of the "
                          "workload's sizes: the practical MFMA ceiling of this chip")
+    ap.add_argument("--sweep", default="",
+                    help="only run the batch sweep of this expert-parallel shard workload "
+                         "(gptoss_shard_bf16): one JSON line per batch size")
+    ap.add_argument("--sweep-block-m", default="",
+                    help="with --sweep: also time each of these block_m values (comma list)")
+    ap.add_argument("--sweep-points", default="",
+                    help="with --sweep: indices into the 48 batch sizes (comma list)")
+    ap.add_argument("--sweep-out", default="", help="with --sweep: write a markdown table here")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this layer runs on one GPU only (no sharding, no collectives); "
@@ -191,6 +319,10 @@ def main():
 
     if args.dense_reference:
         dense_reference(args)
+        return
+
+    if args.sweep:
+        sweep(args)
         return
 
     import routed_grouped_gemm_topk_amd as moe

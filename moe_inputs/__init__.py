@@ -8,12 +8,13 @@ weight block quantisation of the fp8 workload live here because they produce
 the layer's *inputs*: the layer receives expert ids, routing weights and
 already-quantised weights.
 """
-from .configs import CONFIGS, MoEConfig, get_config  # noqa: F401
+from .configs import CONFIGS, SWEEP_CONFIGS, MoEConfig, get_config, sweep_batch_sizes  # noqa: F401
 from .generate import (  # noqa: F401
     MoECase,
     make_case,
     make_logits,
     make_routing,
+    make_x,
     routing_stats,
     slab_seed,
 )

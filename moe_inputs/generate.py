@@ -5,9 +5,11 @@ benchmark):
 
 * Every tensor slab has its own seed ``slab_seed(seed, tag, e)`` derived with
   numpy's SeedSequence from (seed, tag, expert), tag in {X:1, W13:2, W2:3,
-  logits:4, bias:5}.  Slabs can therefore be regenerated one expert at a time.
+  logits:4, bias:5, token clusters:6}.  Slabs can therefore be regenerated one expert at a time.
 * Routing is made on the host in float64 with numpy: logits[T,E] ~ N(0,1),
-  plus a per-expert bias ~ N(0, logit_bias_std) for the skewed workload;
+  plus a per-expert bias ~ N(0, logit_bias_std) for the skewed workload, or
+  for the expert-parallel shard the production-like logits over all E_r
+  experts (recipe in configs.py; Gumbel noise is -log(-log U));
   softmax; the top-k experts in descending probability (ties to the lower
   expert id, so the k experts of a token are distinct); routing weights are the
   chosen probabilities, renormalised to sum 1 only where the workload says so;
@@ -34,9 +36,10 @@ from typing import Optional
 import numpy as np
 import torch
 
+from . import configs as _c
 from .configs import MoEConfig
 
-TAG_X, TAG_W13, TAG_W2, TAG_LOGITS, TAG_BIAS = 1, 2, 3, 4, 5
+TAG_X, TAG_W13, TAG_W2, TAG_LOGITS, TAG_BIAS, TAG_CLUSTER = 1, 2, 3, 4, 5, 6
 E4M3_MAX = 448.0
 
 
@@ -50,11 +53,37 @@ def _rng(seed: int, tag: int, e: int = 0) -> np.random.Generator:
     return np.random.default_rng(slab_seed(seed, tag, e))
 
 
+def _prod_like_logits(cfg: MoEConfig, seed: int, er: int) -> np.ndarray:
+    """Production-like logits [T, er]: expert-level draws (popularity order, clusters, hot
+    experts) come from one stream, per-token draws from two others, so the first T' rows do not
+    depend on T."""
+    g = _rng(seed, TAG_BIAS)
+    ranked = np.arange(1, er + 1, dtype=np.float64) ** -_c.PROD_ZIPF_ALPHA
+    ranked /= ranked.sum()
+    prob = np.empty(er)
+    prob[g.permutation(er)] = ranked
+    size = min(er, max(2 * cfg.top_k, er // 16))
+    clusters = np.stack([g.choice(er, size, replace=False, p=prob)
+                         for _ in range(_c.PROD_CLUSTERS)])
+    hot = g.choice(er, _c.PROD_HOT_EXPERTS, replace=False, p=prob)
+    logits = np.repeat(np.log(np.maximum(prob, 1e-12))[None, :], cfg.T, axis=0)
+    tok_cluster = _rng(seed, TAG_CLUSTER).integers(0, _c.PROD_CLUSTERS, cfg.T)
+    logits[np.arange(cfg.T)[:, None], clusters[tok_cluster]] += _c.PROD_CLUSTER_BOOST
+    logits[:, hot] += _c.PROD_HOT_BOOST
+    u = _rng(seed, TAG_LOGITS).random((cfg.T, er))
+    logits += _c.PROD_GUMBEL_SCALE * -np.log(-np.log(np.clip(u, 1e-300, None)))
+    return logits
+
+
 def make_logits(cfg: MoEConfig, seed: int = 0) -> np.ndarray:
-    """Router logits [T, E] (float64): N(0,1), plus the per-expert bias of the skewed workload."""
-    logits = _rng(seed, TAG_LOGITS).standard_normal((cfg.T, cfg.E))
+    """Router logits [T, E_r] (float64), E_r = cfg.route_experts or E: N(0,1), plus the per-expert
+    bias of the skewed workload; or the production-like logits."""
+    er = cfg.route_experts or cfg.E
+    if cfg.prod_like:
+        return _prod_like_logits(cfg, seed, er)
+    logits = _rng(seed, TAG_LOGITS).standard_normal((cfg.T, er))
     if cfg.logit_bias_std:
-        logits = logits + cfg.logit_bias_std * _rng(seed, TAG_BIAS).standard_normal(cfg.E)[None, :]
+        logits = logits + cfg.logit_bias_std * _rng(seed, TAG_BIAS).standard_normal(er)[None, :]
     return logits
 
 
@@ -84,7 +113,9 @@ def routing_stats(ids: np.ndarray, E: int) -> dict:
     }
 
 
-def _x_host(cfg: MoEConfig, seed: int) -> np.ndarray:
+def make_x(cfg: MoEConfig, seed: int = 0) -> np.ndarray:
+    """X [T, H] on the host (float32, before rounding to the activation dtype); the first T'
+    rows do not depend on T."""
     return _rng(seed, TAG_X).standard_normal((cfg.T, cfg.H), dtype=np.float32)
 
 
@@ -172,7 +203,7 @@ def make_case(cfg: MoEConfig, device="cpu", seed: int = 0, experts=None) -> MoEC
     to a subset (the rest of the weight tensors is left uninitialised)."""
     device = torch.device(device)
     ids, w, _ = make_routing(cfg, seed)
-    xh = _x_host(cfg, seed)
+    xh = make_x(cfg, seed)
     xdt = torch.float32 if cfg.x_dtype == "f32" else torch.bfloat16
     x = torch.from_numpy(xh).to(xdt).to(device)
     w13, s13 = _weights(cfg, TAG_W13, (2 * cfg.I, cfg.H), device, seed, experts)

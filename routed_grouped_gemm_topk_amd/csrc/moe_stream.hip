@@ -76,17 +76,20 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   float acc[L];
   #pragma unroll
   for (int i = 0; i < L; ++i) acc[i] = 0.0f;
-  // slots in batches of 4: every load of a batch is issued before the first add (a slot
-  // with an excluded id was never written, so its vector is loaded but not added)
+  // slots in batches of 4: every row load of a batch is issued before the first add.  A slot
+  // with an excluded id (another shard's expert) was never written and is not read: on an
+  // expert-parallel shard most slots are such.
   constexpr int U = 4;
   for (int j0 = 0; j0 < top_k; j0 += U) {
     int ok[U];
     i32x4 v[U];
     #pragma unroll
+    for (int u = 0; u < U; ++u)
+      ok[u] = (j0 + u < top_k) ? slot_row[(int64_t)t * top_k + j0 + u] >= 0 : 0;
+    #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t s = (int64_t)t * top_k + j0 + u;
-      ok[u] = (j0 + u < top_k) ? slot_row[s] >= 0 : 0;
-      v[u] = (j0 + u < top_k) ? slot_out[s * vec_per_row + c] : i32x4{0, 0, 0, 0};
+      v[u] = ok[u] ? slot_out[s * vec_per_row + c] : i32x4{0, 0, 0, 0};
     }
     #pragma unroll
     for (int u = 0; u < U; ++u) {

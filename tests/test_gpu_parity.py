@@ -482,3 +482,71 @@ def test_forward_full_size_max_dims(device, label):
     assert err <= tol_of(cfg)
     del case
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------------------------
+# the expert-parallel shard of the batch sweep: 16 local experts of 128, so most slots carry ids
+# of other shards (excluded and counted); production-like skew (one expert holds most tokens)
+# ---------------------------------------------------------------------------------------------
+SHARD = "gptoss_shard_bf16"
+SHARD_POINTS = {0: None, 9: None, 20: 48, 47: 24}   # sweep index -> sampled tokens (None: all)
+
+
+@pytest.mark.parametrize("idx", list(SHARD_POINTS))
+def test_shard_sweep_points(device, idx):
+    from moe_inputs import SWEEP_CONFIGS, sweep_batch_sizes
+    base = SWEEP_CONFIGS[SHARD]
+    T = sweep_batch_sizes(base.route_experts, base.top_k)[idx]
+    cfg = get_config(SHARD, T=T)
+    say(f"shard T={T}: generating")
+    case = make_case(cfg, device, seed=0)
+    p = problem_of(cfg)
+    check_alignment(p, case.topk_ids, case.ids_host)
+    out, ws = run_forward(case)
+    torch.cuda.synchronize()
+    n_local = int(((case.ids_host >= 0) & (case.ids_host < cfg.E)).sum())
+    assert int(ws[:4].view(torch.int32).item()) == cfg.T * cfg.top_k - n_local
+    got_all = to_np(out.to(torch.float32))
+    # a token none of whose experts is local gets an exactly zero row (at the smallest batches
+    # every token reaches the hot local expert, so there may be none)
+    foreign = ~((case.ids_host < cfg.E).any(axis=1))
+    assert (got_all[foreign] == 0).all()
+    n = SHARD_POINTS[idx]
+    if n is None:
+        toks = list(range(cfg.T))
+    else:
+        rng = np.random.default_rng(7)
+        counts = np.bincount(case.ids_host.reshape(-1), minlength=cfg.route_experts)[:cfg.E]
+        lo = int(np.argmin(np.where(counts > 0, counts, 1 << 30)))   # least-loaded active expert
+        hot = int(np.argmax(counts))
+        pick = {int(np.nonzero((case.ids_host == e).any(axis=1))[0][-1]) for e in (lo, hot)}
+        local = np.nonzero(~foreign)[0]
+        toks = sorted(set(rng.choice(local, n - 2, replace=False).tolist()) | pick)
+    say(f"shard T={T}: oracle on {len(toks)} tokens (block_m {moe.moe_pick_block_m(p)})")
+    ref = oracle.moe_layer(case.x_host(), case.ids_host, case.w_host, expert_getter(case),
+                           cfg.E, tokens=toks)
+    err = rel_err(got_all[toks], ref)
+    say(f"  rel err {err:.3e}")
+    assert np.isfinite(got_all).all()
+    assert err <= tol_of(cfg)
+    del case
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("bm", [16, 32, 64, 128, 256])
+def test_shard_every_block_m(device, bm):
+    from moe_inputs import SWEEP_CONFIGS, sweep_batch_sizes
+    base = SWEEP_CONFIGS[SHARD]
+    T = sweep_batch_sizes(base.route_experts, base.top_k)[14]
+    cfg = get_config(SHARD, T=T)
+    say(f"shard T={T} block_m {bm}")
+    case = make_case(cfg, device, seed=1)
+    check_alignment(problem_of(cfg, bm), case.topk_ids, case.ids_host)
+    out, _ = run_forward(case, bm)
+    torch.cuda.synchronize()
+    ref = oracle.moe_layer(case.x_host(), case.ids_host, case.w_host, expert_getter(case), cfg.E)
+    err = rel_err(to_np(out.to(torch.float32)), ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= tol_of(cfg)
+    del case
+    torch.cuda.empty_cache()

@@ -126,3 +126,15 @@ def test_agrees_with_the_input_generator(name):
     ids, w = oracle.route(make_logits(cfg, 0), cfg.top_k, cfg.renormalize)
     assert np.array_equal(ids, ids_gen)
     assert np.allclose(w, w_gen, rtol=1e-6, atol=0)
+
+
+def test_agrees_with_the_input_generator_on_the_shard_workload():
+    """Production-like logits over 128 experts (the expert-parallel shard's router)."""
+    from moe_inputs import get_config, make_logits, make_routing
+    cfg = get_config("gptoss_shard_bf16", T=512)
+    ids_gen, w_gen, _ = make_routing(cfg, 0)
+    lg = make_logits(cfg, 0)
+    assert lg.shape == (512, 128)
+    ids, w = oracle.route(lg, cfg.top_k, cfg.renormalize)
+    assert np.array_equal(ids, ids_gen)
+    assert np.allclose(w, w_gen, rtol=1e-6, atol=0)
