@@ -157,9 +157,10 @@ def dense_reference(args):
 def sweep(args):
     """The 48-point batch sweep of one expert-parallel shard ("MOE Bmm1 Fused Gather", its bench:
     batch sizes and production-like routing).  Per batch size: the whole layer (align, up, down,
-    combine) at the library's block_m, and optionally at each block_m of --sweep-block-m; one JSON
-    line per point with the up kernel's and the layer's times, useful TFLOP/s (local slots only)
-    and the up kernel's roofline fraction max(flops/peak, bytes/HBM peak) / time."""
+    combine) at the block_m an expert-parallel caller gets from moe_block_m_for(T*k/E_total)
+    (or --block-m), and optionally at each block_m of --sweep-block-m; one JSON line per point
+    with the up kernel's and the layer's times, useful TFLOP/s (local slots only) and the up
+    kernel's roofline fraction max(flops/peak, bytes/HBM peak) / time."""
     import numpy as np
     import torch
 
@@ -228,12 +229,16 @@ def sweep(args):
             return bm_used, {"align": st(0, 1), "up": st(1, 2), "down": st(2, 3),
                              "combine": st(3, 4), "layer": st(0, 4)}
 
-        bm0, t0 = run(args.block_m)
+        bm_ep = args.block_m or moe.moe_block_m_for(T * K / (base.route_experts or E), "bf16",
+                                                    base.w_dtype)
+        bm0, t0 = run(bm_ep)
         best = None
+        by_bm = {}
         for bm in cands:
             if bm == 256 and base.w_dtype != "bf16":
                 continue
             _, t = run(bm)
+            by_bm[bm] = round(t["layer"], 5)
             if best is None or t["layer"] < best[1]["layer"]:
                 best = (bm, t)
         pt = {"sweep": base.name, "T": T, "tokens_per_expert": T * K // (base.route_experts or E),
@@ -248,6 +253,7 @@ def sweep(args):
             pt["best_block_m"] = best[0]
             pt["best_layer_ms"] = round(best[1]["layer"], 5)
             pt["best_up_ms"] = round(best[1]["up"], 5)
+            pt["layer_ms_by_block_m"] = by_bm
         print(json.dumps(pt), flush=True)
         rows_md.append(pt)
         del ids, wts

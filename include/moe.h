@@ -88,12 +88,20 @@ const char* moe_status_str(int status);
  * points would return for it. */
 int moe_validate(const moe_problem* p);
 
-/* Rows per m-block the library uses for `p` (p->block_m if non-zero, else a
- * choice from the expected slots per expert T*top_k/E and the dtype, in the
- * manner of the block-size table of "MOE Bmm1 Fused Gather"
- * (_select_base_config): few slots per expert -> small blocks).  Returns a
- * negative moe_status for an invalid problem. */
+/* Rows per m-block the library uses for `p` (p->block_m if non-zero, else
+ * moe_block_m_for(T*top_k/E, dtype, w_dtype)).  Returns a negative moe_status
+ * for an invalid problem. */
 int32_t moe_pick_block_m(const moe_problem* p);
+
+/* The library's block size for `slots_per_expert` expected slots per expert, in
+ * the manner of the block-size table of "MOE Bmm1 Fused Gather"
+ * (_select_base_config, keyed on the expected slice size): few slots per expert
+ * -> small blocks.  moe_pick_block_m assumes every id is a local expert; a
+ * caller whose ids mostly belong to other shards (expert parallelism: E local of
+ * E_total experts) passes T*top_k/E_total here and sets block_m to the result.
+ * Host only, no side effects.  MOE_ERR_DTYPE for an unsupported dtype pair,
+ * MOE_ERR_SHAPE for a negative or NaN count. */
+int32_t moe_block_m_for(double slots_per_expert, int32_t dtype, int32_t w_dtype);
 
 /* Upper bound on rows of the padded expert-sorted slot list:
  * N + min(E, N) * (block_m - 1).  Negative moe_status if invalid. */

@@ -95,6 +95,9 @@ SWEEP_CONFIGS = {
                   x_dtype="bf16", renormalize=True, route_experts=128, prod_like=True,
                   description="one expert-parallel shard (16 of 128 experts) of a GPT-OSS-120B-"
                               "shaped MoE layer, bf16, top-4 of 128, production-like skew"),
+        MoEConfig("gptoss_shard_uniform_bf16", T=31744, H=2880, I=2880, E=16, top_k=4,
+                  w_dtype="bf16", x_dtype="bf16", renormalize=True, route_experts=128,
+                  description="the same shard with logits ~N(0,1) (the bench's uniform routing)"),
     ]
 }
 

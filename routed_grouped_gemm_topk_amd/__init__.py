@@ -29,6 +29,7 @@ from ._lib import (  # noqa: F401
     load,
     make_problem,
     moe_align,
+    moe_block_m_for,
     moe_combine,
     moe_forward,
     moe_grouped_gemm_down,

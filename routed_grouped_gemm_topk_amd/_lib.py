@@ -29,7 +29,7 @@ MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 _DT_NAME = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_E4M3}
 _TORCH_DT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_E4M3: torch.float8_e4m3fn}
 
-EXPORTS = ["moe_status_str", "moe_validate", "moe_pick_block_m", "moe_max_padded_slots",
+EXPORTS = ["moe_status_str", "moe_validate", "moe_pick_block_m", "moe_block_m_for", "moe_max_padded_slots",
            "moe_max_tiles", "moe_workspace_bytes", "moe_route", "moe_route_align", "moe_align",
            "moe_quantize_rows_e4m3", "moe_grouped_gemm_up", "moe_grouped_gemm_down",
            "moe_combine", "moe_forward"]
@@ -78,6 +78,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_validate": (ctypes.c_int, [P]),
         "moe_pick_block_m": (i32, [P]),
+        "moe_block_m_for": (i32, [ctypes.c_double, i32, i32]),
         "moe_max_padded_slots": (ctypes.c_int64, [P]),
         "moe_max_tiles": (ctypes.c_int64, [P]),
         "moe_workspace_bytes": (ctypes.c_int64, [P]),
@@ -118,6 +119,12 @@ def _checked(v: int, where: str) -> int:
 
 def moe_pick_block_m(p: Problem) -> int:
     return _checked(load().moe_pick_block_m(ctypes.byref(p)), "moe_pick_block_m")
+
+
+def moe_block_m_for(slots_per_expert: float, dtype="bf16", w_dtype=None) -> int:
+    dt = _DT_NAME[dtype] if isinstance(dtype, str) else int(dtype)
+    wdt = dt if w_dtype is None else (_DT_NAME[w_dtype] if isinstance(w_dtype, str) else int(w_dtype))
+    return _checked(load().moe_block_m_for(float(slots_per_expert), dt, wdt), "moe_block_m_for")
 
 
 def moe_max_padded_slots(p: Problem) -> int:

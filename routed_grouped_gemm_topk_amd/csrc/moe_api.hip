@@ -18,19 +18,29 @@ int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 int elt_bytes(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 2 : 1; }
 
-int32_t choose_block_m(const moe_problem* p) {
-  if (p->block_m) return p->block_m;
-  // Expected slots per expert, m = T*top_k/E.  Few slots per expert: the m-block
-  // should hold a whole expert so each weight tile is streamed from HBM once;
-  // many slots: large m-blocks keep the MFMA tiles large.  bf16 experts with hundreds
-  // of slots take 256-row blocks (fewer bytes per flop through LDS; the extra padding
-  // of an expert's last block is at most 255 rows).
-  const double m = (double)p->T * p->top_k / p->E;
+// Rows per m-block for m expected slots per expert.  Few slots per expert: the m-block should
+// hold a whole expert so each weight tile is streamed from HBM once; many slots: large
+// m-blocks keep the MFMA tiles large (fewer bytes per flop through LDS; the padding of an
+// expert's last block grows with the block).  The bf16 thresholds are where the measured
+// best block size changes in a batch sweep with uniform routing over 16 experts of
+// H = I = 2880 (16 up to 10 slots, 32 up to 28, 64 up to 64, 128 up to 128, then 256).
+int32_t block_m_for(double m, int dtype, int w_dtype) {
+  if (dtype == MOE_BF16 && w_dtype == MOE_BF16) {
+    if (m <= 10) return 16;
+    if (m <= 28) return 32;
+    if (m <= 64) return 64;
+    if (m <= 128) return 128;
+    return 256;
+  }
   if (m <= 8) return 16;
   if (m <= 20) return 32;
   if (m <= 40) return 64;
-  if (m >= 512 && p->dtype == MOE_BF16 && p->w_dtype == MOE_BF16) return 256;
   return 128;
+}
+
+int32_t choose_block_m(const moe_problem* p) {
+  if (p->block_m) return p->block_m;
+  return block_m_for((double)p->T * p->top_k / p->E, p->dtype, p->w_dtype);
 }
 
 int validate(const moe_problem* p) {
@@ -141,6 +151,14 @@ int moe_validate(const moe_problem* p) { return validate(p); }
 int32_t moe_pick_block_m(const moe_problem* p) {
   const int v = validate(p);
   return v != MOE_OK ? v : choose_block_m(p);
+}
+
+int32_t moe_block_m_for(double slots_per_expert, int32_t dtype, int32_t w_dtype) {
+  const bool ok = (dtype == MOE_F32 && w_dtype == MOE_F32) ||
+                  (dtype == MOE_BF16 && (w_dtype == MOE_BF16 || w_dtype == MOE_E4M3));
+  if (!ok) return MOE_ERR_DTYPE;
+  if (!(slots_per_expert >= 0.0)) return MOE_ERR_SHAPE;      // negative or NaN
+  return block_m_for(slots_per_expert, dtype, w_dtype);
 }
 
 int64_t moe_max_padded_slots(const moe_problem* p) {

@@ -384,8 +384,8 @@ hipError_t launch_up(const Resolved& r, const void* x, const float* x_scales, co
   if (prefill_supported(r))
     return launch_up_prefill(r, x, w13, sorted_slots, offsets, tiles, num_tiles, act, s);
   if (stream_supported(r))
-    return launch_up_stream(r, x, x_scales, w13, w13_scales, sorted_slots, tiles, num_tiles, act,
-                            act_scales, s);
+    return launch_up_stream(r, x, x_scales, w13, w13_scales, sorted_slots, offsets, tiles,
+                            num_tiles, act, act_scales, s);
   GemmArgs a{};
   a.a_src = (const char*)x;
   a.a_scales = x_scales;
@@ -416,8 +416,8 @@ hipError_t launch_down(const Resolved& r, const void* act, const float* act_scal
     return launch_down_prefill(r, act, w2, topk_w, sorted_slots, offsets, tiles, num_tiles,
                                slot_out, s);
   if (stream_supported(r))
-    return launch_down_stream(r, act, act_scales, w2, w2_scales, topk_w, sorted_slots, tiles,
-                              num_tiles, slot_out, s);
+    return launch_down_stream(r, act, act_scales, w2, w2_scales, topk_w, sorted_slots, offsets,
+                              tiles, num_tiles, slot_out, s);
   GemmArgs a{};
   a.a_src = (const char*)act;
   a.a_scales = act_scales;

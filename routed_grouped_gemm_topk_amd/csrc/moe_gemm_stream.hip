@@ -28,6 +28,8 @@ namespace moe {
 
 namespace st {
 
+constexpr int kGroupM = 4;   // m-blocks of one expert that sweep the n-blocks together
+
 constexpr int ROWB = 128;   // bytes per row per k-slice
 constexpr int WN = 4;       // waves side by side along N (times WM waves along M)
 
@@ -42,6 +44,7 @@ struct Args {
   const char* w;              // up: W13 [E, 2I, K]; down: W2 [E, H, K]
   const float* w_scales;      // e4m3: [E, w_rows/128, K/128]
   const int32_t* sorted_slots;
+  const int32_t* offsets;
   const int32_t* tiles;
   const int32_t* num_tiles;
   const float* topk_w;        // down
@@ -87,16 +90,18 @@ __global__ __launch_bounds__(WN * WM * kWave) void stream_kernel(Args g) {
   const int wn = wave % WN;
   const int wm = wave / WN;
 
-  // ---- tile: n-block fastest.  At these block sizes an expert has about one m-block, so
-  // workgroups share no weights; what they can share is the m-block's gathered A rows, which
-  // the n-blocks of one m-block (adjacent logical tiles, so on one XCD at the same time) read
-  // from that XCD's L2 instead of HBM. ------------------------------------------------------
+  // ---- tile: expert by expert, groups of kGroupM m-blocks sweep the n-blocks.  At these
+  // block sizes an expert usually has about one m-block, so the order is n-block fastest and
+  // what workgroups share is the m-block's gathered A rows, which the n-blocks of one m-block
+  // (adjacent logical tiles, so on one XCD at the same time) read from that XCD's L2.  An
+  // expert with many slots (a hot expert) has many m-blocks; grouping them lets each weight
+  // tile serve kGroupM m-blocks from L2 (measured 14-20% faster on such batches). ------------
   const int ntiles = *g.num_tiles;
   const int nblk = g.n_out / BNA;
   const int logical = xcd_logical(blockIdx.x, ntiles * nblk);
   if (logical < 0) return;
-  const int mt = logical / nblk;
-  const int nt = logical % nblk;
+  int mt, nt;
+  grouped_tile<BM, kGroupM>(logical, nblk, g.tiles, g.offsets, mt, nt);
   const int e = g.tiles[2 * mt];
   const int row0 = g.tiles[2 * mt + 1];
   const int n0 = nt * BNA;
@@ -415,14 +420,15 @@ bool stream_supported(const Resolved& r) {
 
 hipError_t launch_up_stream(const Resolved& r, const void* x, const float* x_scales,
                             const void* w13, const float* w13_scales, const int32_t* sorted_slots,
-                            const int32_t* tiles, const int32_t* num_tiles, void* act,
-                            float* act_scales, hipStream_t s) {
+                            const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles,
+                            void* act, float* act_scales, hipStream_t s) {
   st::Args a{};
   a.a_src = (const char*)x;
   a.a_scales = x_scales;
   a.w = (const char*)w13;
   a.w_scales = w13_scales;
   a.sorted_slots = sorted_slots;
+  a.offsets = offsets;
   a.tiles = tiles;
   a.num_tiles = num_tiles;
   a.out = act;
@@ -457,14 +463,16 @@ hipError_t launch_up_stream(const Resolved& r, const void* x, const float* x_sca
 
 hipError_t launch_down_stream(const Resolved& r, const void* act, const float* act_scales,
                               const void* w2, const float* w2_scales, const float* topk_w,
-                              const int32_t* sorted_slots, const int32_t* tiles,
-                              const int32_t* num_tiles, void* slot_out, hipStream_t s) {
+                              const int32_t* sorted_slots, const int32_t* offsets,
+                              const int32_t* tiles, const int32_t* num_tiles, void* slot_out,
+                              hipStream_t s) {
   st::Args a{};
   a.a_src = (const char*)act;
   a.a_scales = act_scales;
   a.w = (const char*)w2;
   a.w_scales = w2_scales;
   a.sorted_slots = sorted_slots;
+  a.offsets = offsets;
   a.tiles = tiles;
   a.num_tiles = num_tiles;
   a.topk_w = topk_w;

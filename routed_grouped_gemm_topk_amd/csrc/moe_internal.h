@@ -126,6 +126,49 @@ __device__ __forceinline__ int xcd_logical(int b, int valid) {
   return l < valid ? l : -1;
 }
 
+// Logical tile order, expert by expert: inside expert e (m-blocks base..base+M-1) groups of
+// G m-blocks sweep the n-blocks, n-block-major inside a group.  A group never holds two
+// experts, so concurrent workgroups of one XCD share their weight tiles (each fetched once)
+// and their gathered rows.  With one m-block per expert this is n-block order.
+// logical / n_blocks is an m-block of the expert that owns `logical`.
+template <int BMT, int G>
+__device__ __forceinline__ void grouped_tile(int logical, int n_blocks, const int32_t* tiles,
+                                             const int32_t* offsets, int& mt, int& nt) {
+  const int e = tiles[2 * (logical / n_blocks)];
+  const int base = offsets[e] / BMT;
+  const int M = (offsets[e + 1] - offsets[e]) / BMT;
+  const int r = logical - base * n_blocks;          // 0 <= r < M * n_blocks
+  const int full = M / G;
+  if (r < full * G * n_blocks) {
+    const int g = r / (G * n_blocks), w = r - g * G * n_blocks;
+    nt = w / G;
+    mt = base + g * G + (w - nt * G);
+  } else {
+    const int rem = M - full * G, w = r - full * G * n_blocks;
+    nt = w / rem;
+    mt = base + full * G + (w - nt * rem);
+  }
+}
+
+// Block b -> logical tile, in chunks: the logical order is cut into chunks of C tiles that are
+// dealt to the XCDs in turn (chunk c to XCD c mod 8), and each XCD runs its chunks in order.
+// A chunk keeps tiles that share operands on one L2 at the same time; dealing them in turn
+// spreads expensive and cheap parts of the order (a hot expert, the padded last m-blocks of
+// small experts) over all XCDs.  The grid must be xcd_chunked_grid(tile bound).
+template <int C>
+__device__ __forceinline__ int xcd_chunked(int b, int valid) {
+  const int x = b & 7, i = b >> 3;
+  const int l = ((i / C) * 8 + x) * C + (i % C);
+  return l < valid ? l : -1;
+}
+
+// Grid for xcd_chunked<C> over at most g logical tiles: every XCD gets as many whole chunks
+// of block positions as the XCD with the most chunks needs.
+template <int C>
+inline int64_t xcd_chunked_grid(int64_t g) {
+  return ((g + C - 1) / C + 7) / 8 * 8 * C;
+}
+
 // Direct-to-LDS copies (gfx950 global_load_lds_dwordx4 / _dword): each wave instruction lands
 // 64 lanes x 16 (or 4) bytes contiguously in LDS at M0.  Issued from inline assembly with
 // explicit vmcnt waits: the compiler's own tracking of LDS DMA makes every LDS read wait for
@@ -201,12 +244,13 @@ hipError_t launch_down_prefill(const Resolved& r, const void* act, const void* w
 bool stream_supported(const Resolved& r);
 hipError_t launch_up_stream(const Resolved& r, const void* x, const float* x_scales,
                             const void* w13, const float* w13_scales, const int32_t* sorted_slots,
-                            const int32_t* tiles, const int32_t* num_tiles, void* act,
-                            float* act_scales, hipStream_t s);
+                            const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles,
+                            void* act, float* act_scales, hipStream_t s);
 hipError_t launch_down_stream(const Resolved& r, const void* act, const float* act_scales,
                               const void* w2, const float* w2_scales, const float* topk_w,
-                              const int32_t* sorted_slots, const int32_t* tiles,
-                              const int32_t* num_tiles, void* slot_out, hipStream_t s);
+                              const int32_t* sorted_slots, const int32_t* offsets,
+                              const int32_t* tiles, const int32_t* num_tiles, void* slot_out,
+                              hipStream_t s);
 
 hipError_t launch_combine(const Resolved& r, const void* slot_out, const int32_t* slot_row,
                           void* out, hipStream_t s);

@@ -102,7 +102,8 @@ def test_entry_points_reject_before_any_hip_call(lib):
 @pytest.mark.parametrize("T,H,I,E,k,dt,wdt,bm", [
     (16, 128, 256, 8, 2, "f32", "f32", 16), (4096, 4096, 14336, 8, 2, "bf16", "bf16", 256),
     (64, 7168, 2048, 256, 8, "bf16", "bf16", 16), (8192, 2048, 1408, 64, 6, "bf16", "bf16", 256),
-    (2048, 4096, 1024, 8, 1, "bf16", "bf16", 128), (4096, 4096, 1024, 8, 1, "f32", "f32", 128),
+    (2048, 4096, 1024, 8, 1, "bf16", "bf16", 256), (1024, 4096, 1024, 8, 1, "bf16", "bf16", 128),
+    (4096, 4096, 1024, 8, 1, "f32", "f32", 128), (640, 2880, 2880, 16, 1, "bf16", "bf16", 64),
     (2048, 7168, 2048, 256, 8, "bf16", "e4m3", 128), (1, 128, 128, 4, 1, "bf16", "bf16", 16),
 ])
 def test_block_m_choice_and_bounds(T, H, I, E, k, dt, wdt, bm):
@@ -115,6 +116,28 @@ def test_block_m_choice_and_bounds(T, H, I, E, k, dt, wdt, bm):
         assert moe.moe_pick_block_m(q) == forced
         assert moe.moe_max_tiles(q) == oracle.max_tiles(T * k, E, forced)
     assert moe.moe_workspace_bytes(p) % 256 == 0
+
+
+def test_block_m_for_expected_slots():
+    """The rule behind moe_pick_block_m, keyed on expected slots per expert; an
+    expert-parallel caller passes T*top_k/E_total."""
+    bf = [(1, 16), (10, 16), (10.5, 32), (28, 32), (29, 64), (64, 64), (65, 128), (128, 128),
+          (129, 256), (1e6, 256), (0, 16)]
+    for m, bm in bf:
+        assert moe.moe_block_m_for(m, "bf16") == bm, m
+    for m, bm in [(8, 16), (20, 32), (40, 64), (41, 128), (1e6, 128)]:
+        assert moe.moe_block_m_for(m, "bf16", "e4m3") == bm
+        assert moe.moe_block_m_for(m, "f32") == bm
+    for T, H, I, E, k, dt, wdt in [(4096, 4096, 14336, 8, 2, "bf16", "bf16"),
+                                   (2048, 7168, 2048, 256, 8, "bf16", "e4m3"),
+                                   (333, 2880, 2880, 16, 4, "bf16", "bf16"), (16, 128, 256, 8, 2, "f32", "f32")]:
+        p = moe.make_problem(T, H, I, E, k, dt, wdt)
+        assert moe.moe_pick_block_m(p) == moe.moe_block_m_for(T * k / E, dt, wdt)
+    lib = moe.load()
+    assert lib.moe_block_m_for(-1.0, moe.MOE_BF16, moe.MOE_BF16) == moe.MOE_ERR_SHAPE
+    assert lib.moe_block_m_for(float("nan"), moe.MOE_BF16, moe.MOE_BF16) == moe.MOE_ERR_SHAPE
+    assert lib.moe_block_m_for(4.0, moe.MOE_F32, moe.MOE_BF16) == moe.MOE_ERR_DTYPE
+    assert lib.moe_block_m_for(4.0, moe.MOE_E4M3, moe.MOE_E4M3) == moe.MOE_ERR_DTYPE
 
 
 def test_binding_rejects_host_tensors():
