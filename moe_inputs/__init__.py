@@ -11,7 +11,10 @@ already-quantised weights.
 from .configs import CONFIGS, SWEEP_CONFIGS, MoEConfig, get_config, sweep_batch_sizes  # noqa: F401
 from .generate import (  # noqa: F401
     MoECase,
+    MXCase,
     make_case,
+    make_mx_case,
+    mx_quantize,
     make_logits,
     make_routing,
     make_x,

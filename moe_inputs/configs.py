@@ -15,8 +15,8 @@ class MoEConfig:
     I: int            # expert intermediate size
     E: int            # experts
     top_k: int
-    w_dtype: str      # "f32" | "bf16" | "e4m3"  (expert weights)
-    x_dtype: str      # "f32" | "bf16"           (hidden states and layer output)
+    w_dtype: str      # "f32" | "bf16" | "e4m3" | "mxfp4"  (expert weights)
+    x_dtype: str      # "f32" | "bf16" | "e4m3" (mxfp4 only: the gathered activations)
     renormalize: bool  # routing weights renormalised to sum 1 over the chosen experts
     logit_bias_std: float = 0.0  # per-expert router bias ~ N(0, std), skews expert loads
     route_experts: int = 0  # ids are drawn over this many experts (0: E); ids >= E belong to
@@ -95,6 +95,10 @@ SWEEP_CONFIGS = {
                   x_dtype="bf16", renormalize=True, route_experts=128, prod_like=True,
                   description="one expert-parallel shard (16 of 128 experts) of a GPT-OSS-120B-"
                               "shaped MoE layer, bf16, top-4 of 128, production-like skew"),
+        MoEConfig("gptoss_shard_mxfp4", T=31744, H=2880, I=2880, E=16, top_k=4, w_dtype="mxfp4",
+                  x_dtype="e4m3", renormalize=True, route_experts=128, prod_like=True,
+                  description="the same shard's first expert GEMM as the page runs it: MXFP4 "
+                              "weights x e4m3 activations, bias, GPT-OSS SwiGLU, e4m3 output"),
         MoEConfig("gptoss_shard_uniform_bf16", T=31744, H=2880, I=2880, E=16, top_k=4,
                   w_dtype="bf16", x_dtype="bf16", renormalize=True, route_experts=128,
                   description="the same shard with logits ~N(0,1) (the bench's uniform routing)"),

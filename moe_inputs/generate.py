@@ -213,3 +213,98 @@ def make_case(cfg: MoEConfig, device="cpu", seed: int = 0, experts=None) -> MoEC
                    topk_weights=torch.from_numpy(w).to(device),
                    w13=w13, w2=w2, w13_scales=s13, w2_scales=s2,
                    ids_host=ids, w_host=w)
+
+
+# ---------------------------------------------------------------------------------------------
+# MXFP4 weights x e4m3 activations: the first expert GEMM of "MOE Bmm1 Fused Gather" (its
+# prepare_case), with the GPT-OSS SwiGLU parameters and per-tensor flex scales.
+# ---------------------------------------------------------------------------------------------
+TAG_MX_SCALARS, TAG_BIAS13 = 7, 8
+E2M1_MAX = 6.0
+_E2M1_MAGS = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)     # codes 0..7 (sign in bit 3)
+
+
+def mx_quantize(w: torch.Tensor, block: int = 32):
+    """Input preparation: float rows [R, K] -> (packed e2m1 [R, K/2] uint8, e8m0 scales
+    [R, K/block] uint8) by the OCP MX rule: per block of `block` values along K the shared
+    exponent is floor(log2(amax)) - 2 (2 = the largest e2m1 exponent), clamped to [-127, 127]
+    (an all-zero block gets -127); each value / 2^exponent is rounded to the nearest e2m1 value,
+    ties to the even code, and saturated to +-6.  Element 2i goes to the low nibble of byte i."""
+    R, K = w.shape
+    b = w.float().reshape(R, K // block, block)
+    amax = b.abs().amax(dim=2)
+    ex = torch.where(amax > 0, torch.floor(torch.log2(torch.where(amax > 0, amax, torch.ones_like(amax)))) - 2,
+                     torch.full_like(amax, -127.0)).clamp(-127, 127)
+    q = (b / torch.exp2(ex)[:, :, None]).reshape(R, K)
+    a = q.abs().clamp(max=E2M1_MAX)
+    mags = torch.tensor(_E2M1_MAGS, device=w.device)
+    hi = torch.searchsorted(mags, a.contiguous(), right=False).clamp(max=7)   # first mag >= a
+    lo = (hi - 1).clamp(min=0)
+    d_lo = a - mags[lo]
+    d_hi = mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    mag_code = torch.where(a == mags[hi], hi, torch.where(pick_hi, hi, lo))
+    code = (mag_code | torch.where(torch.signbit(q) & (mag_code > 0), 8, 0)).to(torch.uint8)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).to(torch.uint8)
+    return packed, (ex + 127).to(torch.uint8)
+
+
+@dataclass
+class MXCase:
+    """One MXFP4 problem on ``device``: e4m3 X codes, MXFP4 W13 with interleaved (gate, linear)
+    rows, fp32 bias, GPT-OSS SwiGLU parameters, x and output flex scales."""
+    cfg: MoEConfig
+    seed: int
+    x_codes: torch.Tensor           # [T, H] uint8 (e4m3)
+    topk_ids: torch.Tensor          # [T, k] int32
+    w13: torch.Tensor               # [E, 2I, H/2] uint8: row 2i = gate_i, row 2i+1 = linear_i
+    w13_scales: torch.Tensor        # [E, H/32, 2I] uint8 (e8m0)
+    bias: torch.Tensor              # [E, 2I] float32, same row order
+    x_scale: torch.Tensor           # [1] float32
+    out_scale: torch.Tensor         # [1] float32
+    alpha: float
+    limit: float
+    ids_host: np.ndarray = field(default=None, repr=False)
+
+    def x_codes_host(self) -> np.ndarray:
+        return self.x_codes.cpu().numpy()
+
+    def expert_host(self, e: int):
+        """(packed [2I, H/2], scales [2I, H/32]) of expert e on the host."""
+        return (self.w13[e].cpu().numpy(), self.w13_scales[e].cpu().numpy().T.copy())
+
+    def bias_host(self) -> np.ndarray:
+        return self.bias.cpu().numpy().astype(np.float64)
+
+
+def make_mx_case(cfg: MoEConfig, device="cpu", seed: int = 0, ids: Optional[np.ndarray] = None,
+                 weight_std: Optional[float] = None) -> MXCase:
+    """X ~ N(0,1) rounded to e4m3 (torch's cast); W13 ~ N(0, std) per expert, MX-quantised;
+    bias ~ N(0,1); alpha = 1 + u/5, limit = 1.3 + u/5, x_scale = 0.5 + u, out_scale = 3.5 + u
+    (u ~ U[0,1), the ranges of the page's prepare_case), each rounded to fp32."""
+    device = torch.device(device)
+    if ids is None:
+        ids, _, _ = make_routing(cfg, seed)
+    ids = np.asarray(ids, dtype=np.int32)
+    x = torch.from_numpy(make_x(cfg, seed)).to(device)
+    x_codes = x.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    std = cfg.weight_std if weight_std is None else weight_std
+    E, I2, H = cfg.E, 2 * cfg.I, cfg.H
+    w13 = torch.empty((E, I2, H // 2), dtype=torch.uint8, device=device)
+    sc = torch.empty((E, H // 32, I2), dtype=torch.uint8, device=device)
+    for e in range(E):
+        g = torch.Generator(device=device)
+        g.manual_seed(slab_seed(seed, TAG_W13, e))
+        w = torch.randn((I2, H), generator=g, device=device, dtype=torch.float32) * std
+        p, s = mx_quantize(w)
+        w13[e].copy_(p)
+        sc[e].copy_(s.t())
+        del w
+    bias = torch.from_numpy(_rng(seed, TAG_BIAS13).standard_normal((E, I2)).astype(np.float32)).to(device)
+    u = _rng(seed, TAG_MX_SCALARS).random(4)
+    alpha, limit = float(np.float32(1.0 + u[0] / 5)), float(np.float32(1.3 + u[1] / 5))
+    xs = torch.tensor([0.5 + u[2]], dtype=torch.float32, device=device)
+    ys = torch.tensor([3.5 + u[3]], dtype=torch.float32, device=device)
+    return MXCase(cfg=cfg, seed=seed, x_codes=x_codes, topk_ids=torch.from_numpy(ids).to(device),
+                  w13=w13, w13_scales=sc, bias=bias, x_scale=xs, out_scale=ys, alpha=alpha,
+                  limit=limit, ids_host=ids)

@@ -14,7 +14,9 @@ closed-form worked example), e4m3 codec (all 256 codes, ties, saturation,
 torch's float8_e4m3fn), group quantisation (error bound, amax code), bf16
 rounding (torch's bfloat16 cast), combine order (crafted cancellation), routing
 (worked examples with ties, brute force over expert subsets, the closed form of a
-renormalised pair).  No
+renormalised pair), MXFP4 up projection (e2m1 value list, torch's e8m0 decode, a
+hand-worked packed row, brute-force nearest values of an independent quantiser,
+SwiGLU closed forms and torch's SiLU, a dense torch top-1 computation).  No
 function here is "parity unpinned".
 """
 from .moe_oracle import (  # noqa: F401
@@ -35,4 +37,14 @@ from .moe_oracle import (  # noqa: F401
     quantize_groups_e4m3,
     route,
     silu,
+)
+from .mx_oracle import (  # noqa: F401
+    e2m1_value,
+    e8m0_value,
+    expert_up_mxfp4,
+    gptoss_swiglu,
+    moe_up_mxfp4,
+    mx_decode,
+    quantize_out_e4m3,
+    unpack_e2m1,
 )

@@ -156,3 +156,72 @@ ROUTE_PINS = [tr.test_worked_example_ties_no_renorm, tr.test_worked_example_reno
 def test_route_mutant_is_caught(mutant, monkeypatch):
     monkeypatch.setattr(oracle, "route", mutant)
     assert _some_pin_fails(ROUTE_PINS)
+
+
+# ---------------------------------------------------------------------------------------------
+# MXFP4 up projection
+# ---------------------------------------------------------------------------------------------
+from oracle import mx_oracle as mx  # noqa: E402
+import test_oracle_mx as tm  # noqa: E402
+
+
+def _unpack_swapped(packed):
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b >> 4
+    out[..., 1::2] = b & 0xF
+    return out
+
+
+def _decode_block16(packed, scales, block=32):
+    vals = mx.e2m1_value(mx.unpack_e2m1(packed))
+    sc = mx.e8m0_value(scales)
+    idx = np.minimum(np.arange(vals.shape[-1]) // 16, sc.shape[-1] - 1)
+    return vals * sc[..., idx]
+
+
+def _swiglu_no_plus_one(gate, linear, alpha, limit):
+    g = np.minimum(np.asarray(gate, np.float64), limit)
+    lin = np.clip(np.asarray(linear, np.float64), -limit, limit)
+    return g / (1.0 + np.exp(-alpha * g)) * lin
+
+
+def _swiglu_gate_clamped_both_sides(gate, linear, alpha, limit):
+    g = np.clip(np.asarray(gate, np.float64), -limit, limit)
+    lin = np.clip(np.asarray(linear, np.float64), -limit, limit)
+    return g / (1.0 + np.exp(-alpha * g)) * (lin + 1.0)
+
+
+def _up_pairs_swapped(x_rows, w_packed_e, w_scales_e, bias_e, x_scale, alpha, limit):
+    w = mx.mx_decode(w_packed_e, w_scales_e)
+    h = (np.asarray(x_rows, np.float64) @ w.T) * float(x_scale) + np.asarray(bias_e, np.float64)
+    return mx.gptoss_swiglu(h[:, 1::2], h[:, 0::2], alpha, limit)
+
+
+def _up_bias_unscaled_order(x_rows, w_packed_e, w_scales_e, bias_e, x_scale, alpha, limit):
+    w = mx.mx_decode(w_packed_e, w_scales_e)
+    h = ((np.asarray(x_rows, np.float64) @ w.T) + np.asarray(bias_e, np.float64)) * float(x_scale)
+    return mx.gptoss_swiglu(h[:, 0::2], h[:, 1::2], alpha, limit)
+
+
+MX_MUTANTS = {
+    "nibble_order": ("unpack_e2m1", _unpack_swapped),
+    "scale_block_16": ("mx_decode", _decode_block16),
+    "no_plus_one": ("gptoss_swiglu", _swiglu_no_plus_one),
+    "gate_clamped_below": ("gptoss_swiglu", _swiglu_gate_clamped_both_sides),
+    "gate_linear_swapped": ("expert_up_mxfp4", _up_pairs_swapped),
+    "bias_scaled": ("expert_up_mxfp4", _up_bias_unscaled_order),
+}
+
+MX_PINS = [tm.test_mx_decode_worked_example, tm.test_decode_of_generator_quantiser_is_nearest_value,
+           tm.test_swiglu_closed_forms, tm.test_swiglu_without_limit_is_silu_times_linear_plus_one,
+           tm.test_top1_against_dense_torch, tm.test_invariants]
+
+
+@pytest.mark.parametrize("name", list(MX_MUTANTS))
+def test_mx_mutant_is_caught(name, monkeypatch):
+    attr, fn = MX_MUTANTS[name]
+    monkeypatch.setattr(mx, attr, fn)
+    if hasattr(oracle, attr):
+        monkeypatch.setattr(oracle, attr, fn)
+    assert _some_pin_fails(MX_PINS), f"no pin caught mutant {name}"
