@@ -51,7 +51,9 @@ typedef enum moe_status {
 typedef enum moe_dtype {
   MOE_F32 = 0,   /* IEEE binary32                                                   */
   MOE_BF16 = 1,  /* bfloat16                                                        */
-  MOE_E4M3 = 2   /* OCP FP8 E4M3 ("fn": max 448, no infinities), one byte           */
+  MOE_E4M3 = 2,  /* OCP FP8 E4M3 ("fn": max 448, no infinities), one byte           */
+  MOE_MXFP4 = 3  /* OCP MXFP4: e2m1 values two per byte (the lower K index in the    */
+                 /* low nibble) with one e8m0 scale 2^(c-127) per 32 values along K */
 } moe_dtype;
 
 /*
@@ -62,6 +64,9 @@ typedef enum moe_dtype {
  *                              scale per 128x128 block (dequantised W = code*scale);
  *                              X and act quantised to e4m3 per (row, 128-column
  *                              group) with scale amax/448; bf16 slot rows.
+ *   dtype E4M3, w_dtype MXFP4: only moe_grouped_gemm_up_mxfp4 (and the dtype-free
+ *                              moe_align / moe_route / moe_route_align); block_m
+ *                              at most 128.
  * Limits: 1 <= top_k <= E <= 1024; T >= 1; H and I multiples of 64 (of 128 with E4M3
  *         weights), at most 32768;
  *         T*top_k < 2^31 and per-expert weight slabs < 2^31 bytes.
@@ -194,6 +199,36 @@ int moe_grouped_gemm_up(const moe_problem* p, const void* x, const float* x_scal
                         const void* w13, const float* w13_scales, const int32_t* sorted_slots,
                         const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles,
                         void* act, float* act_scales, void* stream);
+
+/*
+ * moe_grouped_gemm_up_mxfp4 -- the up projection of the "MOE Bmm1 Fused Gather"
+ * example's own variant: MXFP4 weights x e4m3 activations, per-expert bias, the
+ * GPT-OSS SwiGLU and an e4m3 output with a flex scale.  (mma_partition: e2m1 weights
+ * with 32-wide microscales times e4m3 rows; apply_bias_and_scale: acc * x_scale +
+ * bias; _swiglu_step1/2; pack_fp8_out_fragment: RNE and saturation to +-448.)
+ * Problem: dtype MOE_E4M3, w_dtype MOE_MXFP4; H and I multiples of 64; block_m <= 128.
+ * For every valid tile (e, row0) and row r with sorted_slots[r] != sentinel:
+ *   x_r  = X[sorted_slots[r] / top_k]             (e4m3 codes)
+ *   h[n] = x_scale * (W13[e, n, :] . x_r) + bias[e, n],   n in [0, 2I)
+ *   g = min(h[2c], limit),  l = clamp(h[2c+1], -limit, limit)
+ *   act[r, c] = e4m3( g / (1 + exp(-alpha * g)) * (l + 1) / out_scale ),  c in [0, I)
+ * In:  x         uint8 [T, H] e4m3 codes; x_scale fp32 [1] (device)
+ *      w13       uint8 [E, 2I, H/2]: row n holds W13[e, n, :] as e2m1 pairs; rows come in
+ *                (gate, linear) pairs: row 2c is the gate and row 2c+1 the linear part of
+ *                act column c (the page's interleaved columns)
+ *      w13_scales uint8 [E, H/32, 2I]: e8m0 scale of W13[e, n, 32b .. 32b+31] at [e, b, n]
+ *      bias      fp32 [E, 2I], same row order; alpha, limit: host floats; out_scale fp32 [1]
+ *      sorted_slots, offsets, tiles, num_tiles: outputs of moe_align for the same problem
+ * Out: act       uint8 [moe_max_padded_slots, I] e4m3 codes in padded expert-sorted row
+ *                order; padding rows and rows past the last valid tile are not written.
+ * All device pointers 16-byte aligned.  MOE_ERR_DTYPE for any other dtype pair.
+ */
+int moe_grouped_gemm_up_mxfp4(const moe_problem* p, const uint8_t* x, const float* x_scale,
+                              const uint8_t* w13, const uint8_t* w13_scales, const float* bias,
+                              float alpha, float limit, const float* out_scale,
+                              const int32_t* sorted_slots, const int32_t* offsets,
+                              const int32_t* tiles, const int32_t* num_tiles, uint8_t* act,
+                              void* stream);
 
 /*
  * moe_grouped_gemm_down -- down projection with the routing weight in the epilogue.

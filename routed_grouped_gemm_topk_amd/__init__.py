@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     MOE_ERR_SHAPE,
     MOE_ERR_WORKSPACE,
     MOE_F32,
+    MOE_MXFP4,
     MOE_OK,
     MoeError,
     Problem,
@@ -34,6 +35,7 @@ from ._lib import (  # noqa: F401
     moe_forward,
     moe_grouped_gemm_down,
     moe_grouped_gemm_up,
+    moe_grouped_gemm_up_mxfp4,
     moe_max_padded_slots,
     moe_max_tiles,
     moe_pick_block_m,

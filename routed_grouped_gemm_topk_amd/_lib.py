@@ -25,13 +25,14 @@ MOE_ERR_WORKSPACE = -4
 MOE_ERR_LAUNCH = -5
 MOE_ERR_DEVICE = -6
 
-MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
-_DT_NAME = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_E4M3}
+MOE_F32, MOE_BF16, MOE_E4M3, MOE_MXFP4 = 0, 1, 2, 3
+_DT_NAME = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_E4M3, "mxfp4": MOE_MXFP4}
 _TORCH_DT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_E4M3: torch.float8_e4m3fn}
 
 EXPORTS = ["moe_status_str", "moe_validate", "moe_pick_block_m", "moe_block_m_for", "moe_max_padded_slots",
            "moe_max_tiles", "moe_workspace_bytes", "moe_route", "moe_route_align", "moe_align",
-           "moe_quantize_rows_e4m3", "moe_grouped_gemm_up", "moe_grouped_gemm_down",
+           "moe_quantize_rows_e4m3", "moe_grouped_gemm_up", "moe_grouped_gemm_up_mxfp4",
+           "moe_grouped_gemm_down",
            "moe_combine", "moe_forward"]
 
 
@@ -87,6 +88,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "moe_route_align": (ctypes.c_int, [P, vp, ctypes.c_int] + [vp] * 9 + [vp]),
         "moe_quantize_rows_e4m3": (ctypes.c_int, [P, vp, vp, vp, vp]),
         "moe_grouped_gemm_up": (ctypes.c_int, [P] + [vp] * 10 + [vp]),
+        "moe_grouped_gemm_up_mxfp4": (ctypes.c_int, [P] + [vp] * 5 + [ctypes.c_float] * 2
+                                      + [vp] * 6 + [vp]),
         "moe_grouped_gemm_down": (ctypes.c_int, [P] + [vp] * 10 + [vp]),
         "moe_combine": (ctypes.c_int, [P, vp, vp, vp, vp]),
         "moe_forward": (ctypes.c_int, [P] + [vp] * 9 + [ctypes.c_size_t, vp]),
@@ -239,6 +242,27 @@ def moe_grouped_gemm_up(p: Problem, x, x_scales, w13, w13_scales, sorted_slots, 
             _ptr(act_scales, "act_scales", torch.float32, rows * p.I // 128)]
     _checked(load().moe_grouped_gemm_up(ctypes.byref(p), *args, _stream(stream)),
              "moe_grouped_gemm_up")
+
+
+def moe_grouped_gemm_up_mxfp4(p: Problem, x, x_scale, w13, w13_scales, bias, alpha: float,
+                              limit: float, out_scale, sorted_slots, offsets, tiles, num_tiles,
+                              act, stream=None) -> None:
+    rows = moe_max_padded_slots(p)
+    u8 = (torch.uint8, torch.float8_e4m3fn)
+    args = [_ptr(x, "x", u8, p.T * p.H),
+            _ptr(x_scale, "x_scale", torch.float32, 1),
+            _ptr(w13, "w13", torch.uint8, p.E * 2 * p.I * p.H // 2),
+            _ptr(w13_scales, "w13_scales", torch.uint8, p.E * (p.H // 32) * 2 * p.I),
+            _ptr(bias, "bias", torch.float32, p.E * 2 * p.I),
+            ctypes.c_float(alpha), ctypes.c_float(limit),
+            _ptr(out_scale, "out_scale", torch.float32, 1),
+            _ptr(sorted_slots, "sorted_slots", torch.int32, rows),
+            _ptr(offsets, "offsets", torch.int32, p.E + 1),
+            _ptr(tiles, "tiles", torch.int32, 2 * moe_max_tiles(p)),
+            _ptr(num_tiles, "num_tiles", torch.int32, 1),
+            _ptr(act, "act", u8, rows * p.I)]
+    _checked(load().moe_grouped_gemm_up_mxfp4(ctypes.byref(p), *args, _stream(stream)),
+             "moe_grouped_gemm_up_mxfp4")
 
 
 def moe_grouped_gemm_down(p: Problem, act, act_scales, w2, w2_scales, topk_weights, sorted_slots,

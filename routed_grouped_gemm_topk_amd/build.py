@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["moe_api.hip", "moe_align.hip", "moe_stream.hip", "moe_gemm.hip", "moe_gemm_prefill.hip",
-           "moe_gemm_stream.hip", "moe_route.hip"]
+           "moe_gemm_stream.hip", "moe_route.hip", "moe_gemm_mx.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep hipcc from forming packed fp32 VALU ops (v_pk_*_f32).

@@ -18,6 +18,8 @@ int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 int elt_bytes(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 2 : 1; }
 
+bool is_mx(const moe_problem* p) { return p->dtype == MOE_E4M3 && p->w_dtype == MOE_MXFP4; }
+
 // Rows per m-block for m expected slots per expert.  Few slots per expert: the m-block should
 // hold a whole expert so each weight tile is streamed from HBM once; many slots: large
 // m-blocks keep the MFMA tiles large (fewer bytes per flop through LDS; the padding of an
@@ -57,19 +59,19 @@ int validate(const moe_problem* p) {
   const bool f32 = p->dtype == MOE_F32 && p->w_dtype == MOE_F32;
   const bool bf16 = p->dtype == MOE_BF16 && p->w_dtype == MOE_BF16;
   const bool fp8 = p->dtype == MOE_BF16 && p->w_dtype == MOE_E4M3;
-  if (!(f32 || bf16 || fp8)) return MOE_ERR_DTYPE;
+  if (!(f32 || bf16 || fp8 || is_mx(p))) return MOE_ERR_DTYPE;
   if (p->block_m == 256 && !bf16) return MOE_ERR_SHAPE;     // 256-row blocks: bf16 only
   const int64_t N = (int64_t)p->T * p->top_k;
   const int64_t BM = choose_block_m(p);
   const int64_t rows = N + (int64_t)(p->E < N ? p->E : N) * (BM - 1);
-  const int we = elt_bytes(p->w_dtype);
+  const int64_t slab = is_mx(p) ? (int64_t)p->I * p->H : (int64_t)2 * p->I * p->H * elt_bytes(p->w_dtype);
   if (N > kI32Max || rows > kI32Max) return MOE_ERR_SHAPE;
-  if ((int64_t)2 * p->I * p->H * we > kI32Max) return MOE_ERR_SHAPE;       // one expert slab
+  if (slab > kI32Max) return MOE_ERR_SHAPE;                                   // one expert slab
   if ((int64_t)p->T * p->H > kI32Max || rows * p->I > kI32Max * 4 || N * p->H > kI32Max * 4)
     return MOE_ERR_SHAPE;
   // grid bound of the GEMM launches
   const int64_t tiles = rows / BM;
-  const int64_t nb = (p->I > p->H ? p->I : p->H) / 128;
+  const int64_t nb = (p->I > p->H ? p->I : p->H) / 64;
   if (tiles * nb > kI32Max) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
@@ -155,7 +157,8 @@ int32_t moe_pick_block_m(const moe_problem* p) {
 
 int32_t moe_block_m_for(double slots_per_expert, int32_t dtype, int32_t w_dtype) {
   const bool ok = (dtype == MOE_F32 && w_dtype == MOE_F32) ||
-                  (dtype == MOE_BF16 && (w_dtype == MOE_BF16 || w_dtype == MOE_E4M3));
+                  (dtype == MOE_BF16 && (w_dtype == MOE_BF16 || w_dtype == MOE_E4M3)) ||
+                  (dtype == MOE_E4M3 && w_dtype == MOE_MXFP4);
   if (!ok) return MOE_ERR_DTYPE;
   if (!(slots_per_expert >= 0.0)) return MOE_ERR_SHAPE;      // negative or NaN
   return block_m_for(slots_per_expert, dtype, w_dtype);
@@ -173,7 +176,9 @@ int64_t moe_max_tiles(const moe_problem* p) {
 
 int64_t moe_workspace_bytes(const moe_problem* p) {
   const int v = validate(p);
-  return v != MOE_OK ? v : layout(resolve(p)).total;
+  if (v != MOE_OK) return v;
+  if (is_mx(p)) return MOE_ERR_DTYPE;                       // no moe_forward for MXFP4
+  return layout(resolve(p)).total;
 }
 
 int moe_route(const moe_problem* p, const float* logits, int renormalize, int32_t* topk_ids,
@@ -222,7 +227,7 @@ int moe_quantize_rows_e4m3(const moe_problem* p, const void* x, uint8_t* xq, flo
                            void* stream) {
   int v = validate(p);
   if (v) return v;
-  if (p->w_dtype != MOE_E4M3) return MOE_ERR_DTYPE;
+  if (p->w_dtype != MOE_E4M3 || p->dtype != MOE_BF16) return MOE_ERR_DTYPE;
   if (!x || !xq || !scales) return MOE_ERR_NULL;
   if ((v = check_device())) return v;
   return status_of(launch_quant_rows(resolve(p), x, xq, scales, (hipStream_t)stream));
@@ -234,11 +239,30 @@ int moe_grouped_gemm_up(const moe_problem* p, const void* x, const float* x_scal
                         void* act, float* act_scales, void* stream) {
   int v = validate(p);
   if (v) return v;
+  if (is_mx(p)) return MOE_ERR_DTYPE;
   if (!x || !w13 || !sorted_slots || !offsets || !tiles || !num_tiles || !act) return MOE_ERR_NULL;
   if (p->w_dtype == MOE_E4M3 && (!x_scales || !w13_scales || !act_scales)) return MOE_ERR_NULL;
   if ((v = check_device())) return v;
   return status_of(launch_up(resolve(p), x, x_scales, w13, w13_scales, sorted_slots, offsets,
                              tiles, num_tiles, act, act_scales, (hipStream_t)stream));
+}
+
+int moe_grouped_gemm_up_mxfp4(const moe_problem* p, const uint8_t* x, const float* x_scale,
+                              const uint8_t* w13, const uint8_t* w13_scales, const float* bias,
+                              float alpha, float limit, const float* out_scale,
+                              const int32_t* sorted_slots, const int32_t* offsets,
+                              const int32_t* tiles, const int32_t* num_tiles, uint8_t* act,
+                              void* stream) {
+  int v = validate(p);
+  if (v) return v;
+  if (!is_mx(p)) return MOE_ERR_DTYPE;
+  if (!x || !x_scale || !w13 || !w13_scales || !bias || !out_scale || !sorted_slots ||
+      !offsets || !tiles || !num_tiles || !act)
+    return MOE_ERR_NULL;
+  if ((v = check_device())) return v;
+  return status_of(launch_up_mxfp4(resolve(p), x, x_scale, w13, w13_scales, bias, alpha, limit,
+                                   out_scale, sorted_slots, offsets, tiles, num_tiles, act,
+                                   (hipStream_t)stream));
 }
 
 int moe_grouped_gemm_down(const moe_problem* p, const void* act, const float* act_scales,
@@ -248,6 +272,7 @@ int moe_grouped_gemm_down(const moe_problem* p, const void* act, const float* ac
                           void* stream) {
   int v = validate(p);
   if (v) return v;
+  if (is_mx(p)) return MOE_ERR_DTYPE;
   if (!act || !w2 || !topk_weights || !sorted_slots || !offsets || !tiles || !num_tiles ||
       !slot_out)
     return MOE_ERR_NULL;
@@ -262,6 +287,7 @@ int moe_combine(const moe_problem* p, const void* slot_out, const int32_t* slot_
                 void* stream) {
   int v = validate(p);
   if (v) return v;
+  if (is_mx(p)) return MOE_ERR_DTYPE;
   if (!slot_out || !slot_row || !out) return MOE_ERR_NULL;
   if ((v = check_device())) return v;
   return status_of(launch_combine(resolve(p), slot_out, slot_row, out, (hipStream_t)stream));
@@ -273,6 +299,7 @@ int moe_forward(const moe_problem* p, const void* x, const int32_t* topk_ids,
                 size_t workspace_bytes, void* stream) {
   int v = validate(p);
   if (v) return v;
+  if (is_mx(p)) return MOE_ERR_DTYPE;
   if (!x || !topk_ids || !topk_weights || !w13 || !w2 || !out || !workspace) return MOE_ERR_NULL;
   const bool fp8 = p->w_dtype == MOE_E4M3;
   if (fp8 && (!w13_scales || !w2_scales)) return MOE_ERR_NULL;

@@ -1,0 +1,305 @@
+// MXFP4 x e4m3 grouped up GEMM with the GPT-OSS SwiGLU: the first expert GEMM of the
+// "MOE Bmm1 Fused Gather" example's own variant (mma_partition: e2m1 weights with 32-wide
+// microscales times e4m3 activations; apply_bias_and_scale: acc * x_scale + bias;
+// _swiglu_step1/2: (gate, linear) column pairs, gate capped at limit, linear clamped,
+// act = gate / (1 + exp(-alpha * gate)) * (linear + 1); pack_fp8_out_fragment: e4m3 of
+// act / out_scale, round to nearest even, saturating).
+//
+//   act[r, c] = e4m3( swiglu( x_scale * (W13[e, 2c, :] . x_r) + bias[e, 2c],
+//                             x_scale * (W13[e, 2c+1, :] . x_r) + bias[e, 2c+1] ) / out_scale )
+//   x_r = X[sorted_slots[r] / top_k] (e4m3 codes), W13 rows MXFP4 (e2m1 pairs + e8m0 per 32 K)
+//
+// MI355X shape:
+//   * v_mfma_scale_f32_16x16x128_f8f6f4 with the weights as the first operand (format e2m1,
+//     the lane's e8m0 microscale as its scale) and the gathered rows as the second (e4m3,
+//     scale 1.0; x_scale is applied in the epilogue).  Weight rows on the first operand put
+//     four consecutive W13 rows -- two (gate, linear) pairs -- in each lane's result, so the
+//     SwiGLU needs no cross-lane exchange.
+//     Operand layout (measured): the e2m1 lane (l >> 4) = q holds the 32 values of microscale
+//     block q of the 128-value k-step, low nibble first; the e4m3 lane q holds bytes
+//     [16q, 16q + 16) and [64 + 16q, 64 + 16q + 16) of the k-step.
+//   * one 128-value k-step per slice, NS-stage direct-to-LDS ring: per slice BM rows x 128 B
+//     of gathered codes, 2*BNA weight rows x 64 B, and the 4 x 2*BNA scale bytes of the slice
+//     (scales are stored [E, H/32, 2I], so a slice's scales are 4 contiguous runs);
+//   * K need only be a multiple of 64: copies of chunks past K read a static zero area;
+//   * tile order: expert by expert, groups of 4 m-blocks sweep the n-blocks; padding rows
+//     read zeros and their 16-row fragments are skipped; their act rows are not written.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace mx {
+
+constexpr int KS = 128;            // K values per slice (one MFMA k-step)
+constexpr int XB = KS;             // gathered-code bytes per row per slice
+constexpr int WB = KS / 2;         // weight bytes per row per slice
+constexpr int kGroupM = 4;
+constexpr int WN = 4;              // waves along the weight rows (times WM along the m-block)
+
+__device__ __attribute__((aligned(16))) char g_zero[256];
+
+// 16-byte chunk swizzles: 128-byte rows (8 chunks) and 64-byte rows (4 chunks); both make the
+// fragment reads (16 consecutive rows at one chunk) conflict-free.
+__device__ __forceinline__ int swz_x(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_w(int r) { return (r >> 2) & 3; }
+
+struct Args {
+  const uint8_t* x;              // [T, K] e4m3 codes
+  const float* x_scale;          // [1]
+  const uint8_t* w;              // [E, 2I, K/2] e2m1 pairs
+  const uint8_t* w_scales;       // [E, K/32, 2I] e8m0
+  const float* bias;             // [E, 2I]
+  const float* out_scale;        // [1]
+  const int32_t* sorted_slots;
+  const int32_t* offsets;
+  const int32_t* tiles;
+  const int32_t* num_tiles;
+  uint8_t* act;                  // [rows_max, I] e4m3 codes
+  float alpha, limit;
+  int K, I, top_k, n_slots;
+};
+
+template <int BM, int BNA, int NS, int WM>
+__global__ __launch_bounds__(WN * WM * kWave) void mx_up_kernel(Args g) {
+  constexpr int NW = WN * WM;
+  constexpr int WROWS = 2 * BNA;                   // weight rows of the tile
+  constexpr int WTW = WROWS / WN;                  // weight rows per wave
+  constexpr int FW = WTW / 16;
+  constexpr int FM = BM / 16;
+  constexpr int FMW = FM / WM;
+  constexpr int NQ_X = BM * XB / 1024;             // 1 KB copies per slice (8 rows each)
+  constexpr int NQ_W = WROWS * WB / 1024;          // (16 rows each)
+  constexpr int NQ = NQ_X + NQ_W;
+  constexpr int NQW = (NQ + NW - 1) / NW;          // per wave; padded slots repeat a real copy
+  constexpr int NS_REAL = 4 * WROWS / 256;         // 256-byte scale copies per slice
+  constexpr int NSW = (NS_REAL + NW - 1) / NW;
+  constexpr int OPS = NQW + NSW;
+  constexpr int W_OFF = BM * XB;
+  constexpr int S_OFF = W_OFF + WROWS * WB;
+  constexpr int STAGE = S_OFF + 4 * WROWS;
+  static_assert(BM % 16 == 0 && FM % WM == 0 && WTW % 16 == 0, "whole MFMA tiles");
+  static_assert((4 * WROWS) % 256 == 0 && NQ_X >= 1, "whole copies");
+  static_assert(NS >= 2 && (NS - 1) * OPS <= 63, "vmcnt range");
+
+  __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wn = wave % WN;
+  const int wm = wave / WN;
+
+  const int ntiles = *g.num_tiles;
+  const int nblk = g.I / BNA;
+  const int logical = xcd_logical(blockIdx.x, ntiles * nblk);
+  if (logical < 0) return;
+  int mt, nt;
+  grouped_tile<BM, kGroupM>(logical, nblk, g.tiles, g.offsets, mt, nt);
+  const int e = g.tiles[2 * mt];
+  const int row0 = g.tiles[2 * mt + 1];
+  const int n0 = nt * BNA;                         // first act column; weight rows from 2*n0
+  const int K = g.K;
+  const int KT = (K + KS - 1) / KS;
+  const int KB = K / 32;                           // microscale blocks per row
+  const int I2 = 2 * g.I;
+
+  // ---- copies: source of this lane for slice 0, its per-slice byte step, the K offset of
+  // its chunk inside a slice (chunks at or past K read zeros), and whether it is live --------
+  const char* src[NQW];
+  int step[NQW], kof[NQW];
+  bool live[NQW];
+  #pragma unroll
+  for (int i = 0; i < NQW; ++i) {
+    const int q = min(wave * NQW + i, NQ - 1);
+    if (q < NQ_X) {                                // gathered rows: 8 per copy
+      const int r = q * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz_x(r);
+      const int s = g.sorted_slots[row0 + r];
+      live[i] = s < g.n_slots;
+      src[i] = reinterpret_cast<const char*>(g.x) + (size_t)(live[i] ? s / g.top_k : 0) * K + c * 16;
+      step[i] = XB;
+      kof[i] = c * 16;
+    } else {                                       // weight rows: 16 per copy
+      const int r = (q - NQ_X) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ swz_w(r);
+      live[i] = true;
+      src[i] = reinterpret_cast<const char*>(g.w) +
+               ((size_t)e * I2 + 2 * n0 + r) * (size_t)(K / 2) + c * 16;
+      step[i] = WB;
+      kof[i] = c * 32;
+    }
+  }
+  const char* ssrc[NSW];
+  int skb[NSW];
+  #pragma unroll
+  for (int i = 0; i < NSW; ++i) {
+    const int q = min(wave * NSW + i, NS_REAL - 1);
+    const int b = q * 256 + lane * 4;              // byte of the slice's [4][WROWS] scale block
+    skb[i] = b / WROWS;
+    ssrc[i] = reinterpret_cast<const char*>(g.w_scales) +
+              ((size_t)e * KB + skb[i]) * I2 + 2 * n0 + (b % WROWS);
+  }
+  const uint32_t lds_base = lds_u32(lds);
+  auto issue = [&](int buf, int kt) {
+    const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + buf * STAGE);
+    const int k0 = kt * KS;
+    #pragma unroll
+    for (int i = 0; i < NQW; ++i) {
+      const int q = min(wave * NQW + i, NQ - 1);
+      const uint32_t dst = q < NQ_X ? st + q * 1024 : st + W_OFF + (q - NQ_X) * 1024;
+      const bool ok = live[i] && k0 + kof[i] < K;
+      lds_dma16(ok ? src[i] + (size_t)kt * step[i] : g_zero, __builtin_amdgcn_readfirstlane(dst));
+    }
+    #pragma unroll
+    for (int i = 0; i < NSW; ++i) {
+      const int q = min(wave * NSW + i, NS_REAL - 1);
+      const bool ok = 4 * kt + skb[i] < KB;
+      lds_dma4(ok ? ssrc[i] + (size_t)kt * 4 * I2 : g_zero,
+               __builtin_amdgcn_readfirstlane(st + S_OFF + q * 256));
+    }
+  };
+
+  // ---- fragments -----------------------------------------------------------------------------
+  const int fr = lane & 15;
+  const int fq = lane >> 4;
+  // weights: row wn*WTW + f*16 + fr, chunk fq (16 bytes = microscale block fq)
+  int w_off[FW], s_off[FW];
+  #pragma unroll
+  for (int f = 0; f < FW; ++f) {
+    const int r = wn * WTW + f * 16 + fr;
+    w_off[f] = W_OFF + r * WB + ((fq ^ swz_w(r)) << 4);
+    s_off[f] = S_OFF + fq * WROWS + r;
+  }
+  // gathered codes: row fi(i)*16 + fr, chunks fq and 4 + fq
+  auto fi = [&](int i) { return wm + WM * i; };
+  int x_off0[FMW], x_off1[FMW];
+  #pragma unroll
+  for (int i = 0; i < FMW; ++i) {
+    const int r = fi(i) * 16 + fr;
+    x_off0[i] = r * XB + ((fq ^ swz_x(r)) << 4);
+    x_off1[i] = r * XB + (((4 + fq) ^ swz_x(r)) << 4);
+  }
+
+  // 16-row fragments from ceil(valid / 16) on are all padding: skipped
+  int fmv;
+  {
+    int valid = 0;
+    #pragma unroll
+    for (int r0 = 0; r0 < BM; r0 += kWave)
+      valid += __popcll(__ballot(r0 + lane < BM && g.sorted_slots[row0 + min(r0 + lane, BM - 1)] < g.n_slots));
+    fmv = __builtin_amdgcn_readfirstlane((valid + 15) >> 4);
+  }
+
+  f32x4 acc[FW][FMW];
+  #pragma unroll
+  for (int f = 0; f < FW; ++f)
+    #pragma unroll
+    for (int i = 0; i < FMW; ++i) acc[f][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Slices kt+1..kt+NS-2 in flight; the barrier at the top of slice kt publishes it and
+  // retires the stage of slice kt-1, which is refilled at once.
+  #pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(s, min(s, KT - 1));
+  int buf = 0;
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_vmcnt<(NS - 2) * OPS>();
+    __syncthreads();
+    issue(buf == 0 ? NS - 1 : buf - 1, min(kt + NS - 1, KT - 1));   // past the end: repeat, unread
+    const char* stg = lds + buf * STAGE;
+    i32x8 wf[FW];
+    int sc[FW];
+    #pragma unroll
+    for (int f = 0; f < FW; ++f) {
+      const i32x4 v = *reinterpret_cast<const i32x4*>(stg + w_off[f]);
+      wf[f] = i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+      sc[f] = *reinterpret_cast<const uint8_t*>(stg + s_off[f]);
+    }
+    #pragma unroll
+    for (int i = 0; i < FMW; ++i) {
+      if (fi(i) >= fmv) break;
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(stg + x_off0[i]);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(stg + x_off1[i]);
+      const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      #pragma unroll
+      for (int f = 0; f < FW; ++f)
+        acc[f][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[f], xf, acc[f][i], 4, 0, 0,
+                                                                     sc[f], 0, 127);
+    }
+    buf = (buf + 1 == NS) ? 0 : buf + 1;
+  }
+  wait_vmcnt<0>();
+
+  // ---- epilogue: lane holds weight rows 4*fq + v (v = 0..3) of fragment f for token fr:
+  // (gate, linear) of act column c and of column c + 1 -----------------------------------------
+  const float xs = *g.x_scale;
+  const float ys = *g.out_scale;
+  #pragma unroll
+  for (int f = 0; f < FW; ++f) {
+    const int wr = 2 * n0 + wn * WTW + f * 16 + 4 * fq;   // first of this lane's 4 weight rows
+    const f32x4 b = *reinterpret_cast<const f32x4*>(g.bias + (size_t)e * I2 + wr);
+    const int c = wr / 2;
+    #pragma unroll
+    for (int i = 0; i < FMW; ++i) {
+      if (fi(i) >= fmv) break;
+      const int m = fi(i) * 16 + fr;
+      if (g.sorted_slots[row0 + m] >= g.n_slots) continue;
+      uint32_t code[2];
+      #pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const float h_g = fmaf(acc[f][i][2 * p], xs, b[2 * p]);
+        const float h_l = fmaf(acc[f][i][2 * p + 1], xs, b[2 * p + 1]);
+        const float gt = fminf(h_g, g.limit);
+        const float ln = fminf(fmaxf(h_l, -g.limit), g.limit);
+        const float a = gt / (1.0f + expf(-g.alpha * gt));
+        code[p] = f32_to_e4m3(fmaf(a, ln, a) / ys);
+      }
+      *reinterpret_cast<uint16_t*>(g.act + (size_t)(row0 + m) * g.I + c) =
+          (uint16_t)(code[0] | (code[1] << 8));
+    }
+  }
+}
+
+template <int BM, int BNA, int NS, int WM>
+hipError_t run(const Args& a, int64_t tiles_max, hipStream_t s) {
+  const int64_t grid = (tiles_max * (a.I / BNA) + 7) / 8 * 8;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((mx_up_kernel<BM, BNA, NS, WM>), dim3((unsigned)grid), dim3(WN * WM * kWave),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mx
+
+hipError_t launch_up_mxfp4(const Resolved& r, const uint8_t* x, const float* x_scale,
+                           const uint8_t* w13, const uint8_t* w13_scales, const float* bias,
+                           float alpha, float limit, const float* out_scale,
+                           const int32_t* sorted_slots, const int32_t* offsets,
+                           const int32_t* tiles, const int32_t* num_tiles, uint8_t* act,
+                           hipStream_t s) {
+  mx::Args a{};
+  a.x = x;
+  a.x_scale = x_scale;
+  a.w = w13;
+  a.w_scales = w13_scales;
+  a.bias = bias;
+  a.out_scale = out_scale;
+  a.sorted_slots = sorted_slots;
+  a.offsets = offsets;
+  a.tiles = tiles;
+  a.num_tiles = num_tiles;
+  a.act = act;
+  a.alpha = alpha;
+  a.limit = limit;
+  a.K = r.H;
+  a.I = r.I;
+  a.top_k = r.K;
+  a.n_slots = (int)r.N;
+  switch (r.BM) {
+    case 16: return mx::run<16, 64, 6, 1>(a, r.tiles_max, s);
+    case 32: return mx::run<32, 64, 6, 1>(a, r.tiles_max, s);
+    case 64: return mx::run<64, 64, 5, 2>(a, r.tiles_max, s);
+    default: return mx::run<128, 64, 4, 2>(a, r.tiles_max, s);
+  }
+}
+
+}  // namespace moe

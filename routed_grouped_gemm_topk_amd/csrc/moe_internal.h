@@ -252,6 +252,12 @@ hipError_t launch_down_stream(const Resolved& r, const void* act, const float* a
                               const int32_t* tiles, const int32_t* num_tiles, void* slot_out,
                               hipStream_t s);
 
+hipError_t launch_up_mxfp4(const Resolved& r, const uint8_t* x, const float* x_scale,
+                           const uint8_t* w13, const uint8_t* w13_scales, const float* bias,
+                           float alpha, float limit, const float* out_scale,
+                           const int32_t* sorted_slots, const int32_t* offsets,
+                           const int32_t* tiles, const int32_t* num_tiles, uint8_t* act,
+                           hipStream_t s);
 hipError_t launch_combine(const Resolved& r, const void* slot_out, const int32_t* slot_row,
                           void* out, hipStream_t s);
 

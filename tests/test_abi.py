@@ -158,3 +158,30 @@ def test_route_entry_points_validate_on_the_host(lib):
     p = bad()
     assert lib.moe_route(ctypes.byref(p), None, 0, None, None, None) == moe.MOE_ERR_NULL
     assert lib.moe_route_align(ctypes.byref(p), None, 1, *([None] * 10)) == moe.MOE_ERR_NULL
+
+
+def test_mxfp4_problem_validation(lib):
+    """MXFP4 weights x e4m3 rows: only the MX up projection (and the dtype-free alignment and
+    routing) accept the pair; the MX entry point rejects every other pair."""
+    mxp = moe.make_problem(16, 192, 128, 8, 2, "e4m3", "mxfp4")
+    assert moe.moe_validate(mxp) == moe.MOE_OK
+    assert moe.moe_pick_block_m(mxp) == moe.moe_block_m_for(4, "e4m3", "mxfp4") == 16
+    for kw, code in [(dict(block_m=256), moe.MOE_ERR_SHAPE), (dict(H=96), moe.MOE_ERR_SHAPE),
+                     (dict(I=96), moe.MOE_ERR_SHAPE)]:
+        base = dict(T=16, H=192, I=128, E=8, top_k=2, dtype="e4m3", w_dtype="mxfp4")
+        base.update(kw)
+        assert moe.moe_validate(moe.make_problem(**base)) == code, kw
+    assert moe.moe_validate(moe.make_problem(16, 192, 128, 8, 2, "bf16", "mxfp4")) == moe.MOE_ERR_DTYPE
+    P = ctypes.byref(mxp)
+    f = [ctypes.c_void_p(256)] * 16
+    assert lib.moe_workspace_bytes(P) == moe.MOE_ERR_DTYPE
+    assert lib.moe_grouped_gemm_up(P, *f[:10], None) == moe.MOE_ERR_DTYPE
+    assert lib.moe_grouped_gemm_down(P, *f[:10], None) == moe.MOE_ERR_DTYPE
+    assert lib.moe_combine(P, *f[:3], None) == moe.MOE_ERR_DTYPE
+    assert lib.moe_quantize_rows_e4m3(P, *f[:3], None) == moe.MOE_ERR_DTYPE
+    assert lib.moe_forward(P, *f[:9], 10 ** 12, None) == moe.MOE_ERR_DTYPE
+    mxargs = f[:5] + [ctypes.c_float(1.1), ctypes.c_float(1.4)] + f[:6]
+    bf = ctypes.byref(bad())
+    assert lib.moe_grouped_gemm_up_mxfp4(bf, *mxargs, None) == moe.MOE_ERR_DTYPE
+    nulls = [None] * 5 + [ctypes.c_float(1.1), ctypes.c_float(1.4)] + [None] * 6
+    assert lib.moe_grouped_gemm_up_mxfp4(P, *nulls, None) == moe.MOE_ERR_NULL
