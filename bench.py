@@ -169,6 +169,8 @@ def sweep(args):
                             sweep_batch_sizes)
 
     base = SWEEP_CONFIGS[args.sweep]
+    if base.w_dtype == "mxfp4":
+        return sweep_mx(args, base)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"generating {base.name} weights and X[{base.T}, {base.H}] on {torch.cuda.get_device_name(dev)}")
@@ -276,6 +278,101 @@ def sweep(args):
                      r["layer_ms"], r["layer_TFLOP/s"]]
                 if cands:
                     v += [r.get("best_block_m"), r.get("best_layer_ms")]
+                f.write("| " + " | ".join(str(c) for c in v) + " |\n")
+        log(f"wrote {args.sweep_out}")
+
+
+def sweep_mx(args, base):
+    """The page's own bench: its first expert GEMM alone (MXFP4 weights x e4m3 rows, bias,
+    GPT-OSS SwiGLU, e4m3 output) over the 48 batch sizes of one expert-parallel shard.  Per
+    point: moe_align + moe_grouped_gemm_up_mxfp4 at the block size an expert-parallel caller
+    gets from moe_block_m_for(T*k/E_total) (optionally also every --sweep-block-m); TFLOP/s and
+    TB/s by the page's own counts -- flops 2 * n_slots * H * 2I, bytes = gathered rows + the
+    active experts' weights, scales and bias + the e4m3 output."""
+    import numpy as np
+    import torch
+
+    import routed_grouped_gemm_topk_amd as moe
+    from moe_inputs import get_config, make_mx_case, make_routing, sweep_batch_sizes
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"generating {base.name} (T={base.T}) on {torch.cuda.get_device_name(dev)}")
+    case = make_mx_case(base, dev, seed=0)
+    batches = sweep_batch_sizes(base.route_experts, base.top_k)
+    if args.sweep_points:
+        batches = [batches[int(i)] for i in args.sweep_points.split(",")]
+    cands = [int(v) for v in args.sweep_block_m.split(",") if int(v) <= 128] if args.sweep_block_m else []
+    peak_tf = PEAK_TFLOPS["e4m3"]
+    E, H, I, K = base.E, base.H, base.I, base.top_k
+    rows_md = []
+    for T in batches:
+        ids_h, _, _ = make_routing(get_config(base.name, T=T), 0)
+        ids = torch.from_numpy(ids_h).to(dev)
+        counts = np.bincount(ids_h.reshape(-1), minlength=E)[:E]
+        n_loc = int(counts.sum())
+        active = int((counts > 0).sum())
+        flops = 2 * n_loc * H * 2 * I
+        nbytes = n_loc * H + active * (2 * I * H // 2 + 2 * I * H // 32 + 2 * I * 4) + n_loc * I
+        roof_ms = max(flops / (peak_tf * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)) * 1e3
+        x = case.x_codes[:T]
+
+        def run(bm):
+            p = moe.make_problem(T, H, I, E, K, "e4m3", "mxfp4", bm)
+            a = moe.alloc_align(p, dev)
+            act = torch.empty((moe.moe_max_padded_slots(p), I), dtype=torch.uint8, device=dev)
+
+            def step(ev=None):
+                if ev: ev[0].record()
+                moe.moe_align(p, ids, a["counts"], a["offsets"], a["sorted_slots"], a["slot_row"],
+                              a["tiles"], a["num_tiles"], a["n_invalid"])
+                if ev: ev[1].record()
+                moe.moe_grouped_gemm_up_mxfp4(p, x, case.x_scale, case.w13, case.w13_scales, case.bias,
+                                              case.alpha, case.limit, case.out_scale, a["sorted_slots"],
+                                              a["offsets"], a["tiles"], a["num_tiles"], act)
+                if ev: ev[2].record()
+            for _ in range(args.warmup):
+                step()
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            for k in range(args.steps):
+                step(evs[k])
+            torch.cuda.synchronize()
+            st = lambda i, j: float(np.mean([e[i].elapsed_time(e[j]) for e in evs]))  # noqa: E731
+            return moe.moe_pick_block_m(p), {"align": st(0, 1), "up": st(1, 2)}
+
+        bm_ep = args.block_m or moe.moe_block_m_for(T * K / base.route_experts, "e4m3", "mxfp4")
+        bm0, t0 = run(bm_ep)
+        by_bm = {bm: round(run(bm)[1]["up"], 5) for bm in cands}
+        pt = {"sweep": base.name, "T": T, "tokens_per_expert": T * K // base.route_experts,
+              "local_slots": n_loc, "active_experts": active, "max_per_expert": int(counts.max()),
+              "block_m": bm0, "align_ms": round(t0["align"], 5), "up_ms": round(t0["up"], 5),
+              "up_TFLOP/s": round(flops / t0["up"] / 1e9, 1),
+              "up_pct_fp8_peak": round(100 * flops / t0["up"] / 1e9 / peak_tf, 2),
+              "up_TB/s": round(nbytes / t0["up"] / 1e9, 3),
+              "up_roofline_frac": round(roof_ms / t0["up"], 4)}
+        if by_bm:
+            best = min(by_bm, key=by_bm.get)
+            pt.update(best_block_m=best, best_up_ms=by_bm[best], up_ms_by_block_m=by_bm)
+        print(json.dumps(pt), flush=True)
+        rows_md.append(pt)
+        del ids
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            f.write(f"# Batch sweep: {base.name}\n\n{base.description}.\n\n")
+            f.write("Command: `python bench.py " + " ".join(sys.argv[1:]) + "`\n\n")
+            f.write(f"Device: {torch.cuda.get_device_name(dev)}; kernel_source_sha256 "
+                    f"`{kernel_source_digest()}`; times are HIP-event means over {args.steps} steps "
+                    f"after {args.warmup} warmup steps.  Peak: {peak_tf} TFLOP/s (fp8 MFMA), "
+                    f"{PEAK_HBM_GBS / 1000} TB/s.\n\n")
+            hdr = ["T", "tok/exp", "local slots", "max/exp", "bm", "up ms", "TFLOP/s", "% fp8 peak",
+                   "TB/s", "roofline frac"] + (["best bm", "best ms"] if cands else [])
+            f.write("| " + " | ".join(hdr) + " |\n|" + "---|" * len(hdr) + "\n")
+            for r in rows_md:
+                v = [r["T"], r["tokens_per_expert"], r["local_slots"], r["max_per_expert"], r["block_m"],
+                     r["up_ms"], r["up_TFLOP/s"], r["up_pct_fp8_peak"], r["up_TB/s"], r["up_roofline_frac"]]
+                if cands:
+                    v += [r.get("best_block_m"), r.get("best_up_ms")]
                 f.write("| " + " | ".join(str(c) for c in v) + " |\n")
         log(f"wrote {args.sweep_out}")
 

@@ -18,9 +18,10 @@
 //     Operand layout (measured): the e2m1 lane (l >> 4) = q holds the 32 values of microscale
 //     block q of the 128-value k-step, low nibble first; the e4m3 lane q holds bytes
 //     [16q, 16q + 16) and [64 + 16q, 64 + 16q + 16) of the k-step.
-//   * one 128-value k-step per slice, NS-stage direct-to-LDS ring: per slice BM rows x 128 B
-//     of gathered codes, 2*BNA weight rows x 64 B, and the 4 x 2*BNA scale bytes of the slice
-//     (scales are stored [E, H/32, 2I], so a slice's scales are 4 contiguous runs);
+//   * KSL 128-value k-steps per slice (one in the dispatched shapes), NS-stage direct-to-LDS
+//     ring: per slice BM rows x 128 B of gathered codes, 2*BNA weight rows x 64 B, and the
+//     4 x 2*BNA scale bytes of the slice (scales are stored [E, H/32, 2I], so a slice's scales
+//     are 4 contiguous runs);
 //   * K need only be a multiple of 64: copies of chunks past K read a static zero area;
 //   * tile order: expert by expert, groups of 4 m-blocks sweep the n-blocks; padding rows
 //     read zeros and their 16-row fragments are skipped; their act rows are not written.
@@ -30,18 +31,20 @@ namespace moe {
 
 namespace mx {
 
-constexpr int KS = 128;            // K values per slice (one MFMA k-step)
-constexpr int XB = KS;             // gathered-code bytes per row per slice
-constexpr int WB = KS / 2;         // weight bytes per row per slice
+constexpr int KM = 128;            // K values per MFMA k-step
 constexpr int kGroupM = 4;
 constexpr int WN = 4;              // waves along the weight rows (times WM along the m-block)
 
 __device__ __attribute__((aligned(16))) char g_zero[256];
 
-// 16-byte chunk swizzles: 128-byte rows (8 chunks) and 64-byte rows (4 chunks); both make the
-// fragment reads (16 consecutive rows at one chunk) conflict-free.
-__device__ __forceinline__ int swz_x(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int swz_w(int r) { return (r >> 2) & 3; }
+// 16-byte chunk swizzle of rows of RB bytes: chunk c of row r sits at c ^ swz<RB>(r), which
+// puts the fragment reads (16 consecutive rows at one chunk) in 16 distinct 4-bank groups.
+template <int RB>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (RB == 64) return (r >> 2) & 3;
+  else if constexpr (RB == 128) return (r & 7) ^ ((r >> 3) & 1);
+  else return r & 15;
+}
 
 struct Args {
   const uint8_t* x;              // [T, K] e4m3 codes
@@ -59,26 +62,32 @@ struct Args {
   int K, I, top_k, n_slots;
 };
 
-template <int BM, int BNA, int NS, int WM>
+template <int BM, int BNA, int NS, int WM, int KSL>
 __global__ __launch_bounds__(WN * WM * kWave) void mx_up_kernel(Args g) {
+  constexpr int KS = KSL * KM;                     // K values per slice
+  constexpr int XB = KS;                           // gathered-code bytes per row per slice
+  constexpr int WB = KS / 2;                       // weight bytes per row per slice
+  constexpr int SB = KS / 32;                      // scale bytes per weight row per slice
+  constexpr int XR = 1024 / XB;                    // rows per 1 KB copy
+  constexpr int WR = 1024 / WB;
   constexpr int NW = WN * WM;
   constexpr int WROWS = 2 * BNA;                   // weight rows of the tile
   constexpr int WTW = WROWS / WN;                  // weight rows per wave
   constexpr int FW = WTW / 16;
   constexpr int FM = BM / 16;
   constexpr int FMW = FM / WM;
-  constexpr int NQ_X = BM * XB / 1024;             // 1 KB copies per slice (8 rows each)
-  constexpr int NQ_W = WROWS * WB / 1024;          // (16 rows each)
+  constexpr int NQ_X = BM * XB / 1024;             // 1 KB copies per slice
+  constexpr int NQ_W = WROWS * WB / 1024;
   constexpr int NQ = NQ_X + NQ_W;
   constexpr int NQW = (NQ + NW - 1) / NW;          // per wave; padded slots repeat a real copy
-  constexpr int NS_REAL = 4 * WROWS / 256;         // 256-byte scale copies per slice
+  constexpr int NS_REAL = SB * WROWS / 256;        // 256-byte scale copies per slice
   constexpr int NSW = (NS_REAL + NW - 1) / NW;
   constexpr int OPS = NQW + NSW;
   constexpr int W_OFF = BM * XB;
   constexpr int S_OFF = W_OFF + WROWS * WB;
-  constexpr int STAGE = S_OFF + 4 * WROWS;
+  constexpr int STAGE = S_OFF + SB * WROWS;
   static_assert(BM % 16 == 0 && FM % WM == 0 && WTW % 16 == 0, "whole MFMA tiles");
-  static_assert((4 * WROWS) % 256 == 0 && NQ_X >= 1, "whole copies");
+  static_assert((SB * WROWS) % 256 == 0 && BM % XR == 0 && NQ_X >= 1, "whole copies");
   static_assert(NS >= 2 && (NS - 1) * OPS <= 63, "vmcnt range");
 
   __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
@@ -111,17 +120,17 @@ __global__ __launch_bounds__(WN * WM * kWave) void mx_up_kernel(Args g) {
   #pragma unroll
   for (int i = 0; i < NQW; ++i) {
     const int q = min(wave * NQW + i, NQ - 1);
-    if (q < NQ_X) {                                // gathered rows: 8 per copy
-      const int r = q * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ swz_x(r);
+    if (q < NQ_X) {                                // gathered rows: XR per copy
+      const int r = q * XR + lane / (XB / 16);
+      const int c = (lane % (XB / 16)) ^ swz<XB>(r);
       const int s = g.sorted_slots[row0 + r];
       live[i] = s < g.n_slots;
       src[i] = reinterpret_cast<const char*>(g.x) + (size_t)(live[i] ? s / g.top_k : 0) * K + c * 16;
       step[i] = XB;
       kof[i] = c * 16;
-    } else {                                       // weight rows: 16 per copy
-      const int r = (q - NQ_X) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ swz_w(r);
+    } else {                                       // weight rows: WR per copy
+      const int r = (q - NQ_X) * WR + lane / (WB / 16);
+      const int c = (lane % (WB / 16)) ^ swz<WB>(r);
       live[i] = true;
       src[i] = reinterpret_cast<const char*>(g.w) +
                ((size_t)e * I2 + 2 * n0 + r) * (size_t)(K / 2) + c * 16;
@@ -134,7 +143,7 @@ __global__ __launch_bounds__(WN * WM * kWave) void mx_up_kernel(Args g) {
   #pragma unroll
   for (int i = 0; i < NSW; ++i) {
     const int q = min(wave * NSW + i, NS_REAL - 1);
-    const int b = q * 256 + lane * 4;              // byte of the slice's [4][WROWS] scale block
+    const int b = q * 256 + lane * 4;              // byte of the slice's [SB][WROWS] scale block
     skb[i] = b / WROWS;
     ssrc[i] = reinterpret_cast<const char*>(g.w_scales) +
               ((size_t)e * KB + skb[i]) * I2 + 2 * n0 + (b % WROWS);
@@ -153,8 +162,8 @@ __global__ __launch_bounds__(WN * WM * kWave) void mx_up_kernel(Args g) {
     #pragma unroll
     for (int i = 0; i < NSW; ++i) {
       const int q = min(wave * NSW + i, NS_REAL - 1);
-      const bool ok = 4 * kt + skb[i] < KB;
-      lds_dma4(ok ? ssrc[i] + (size_t)kt * 4 * I2 : g_zero,
+      const bool ok = SB * kt + skb[i] < KB;
+      lds_dma4(ok ? ssrc[i] + (size_t)kt * SB * I2 : g_zero,
                __builtin_amdgcn_readfirstlane(st + S_OFF + q * 256));
     }
   };
@@ -162,23 +171,21 @@ __global__ __launch_bounds__(WN * WM * kWave) void mx_up_kernel(Args g) {
   // ---- fragments -----------------------------------------------------------------------------
   const int fr = lane & 15;
   const int fq = lane >> 4;
-  // weights: row wn*WTW + f*16 + fr, chunk fq (16 bytes = microscale block fq)
+  // weights, k-step kk: row wn*WTW + f*16 + fr, chunk 4kk + fq (16 bytes = microscale block
+  // 4kk + fq of the slice); the swizzle of a fragment's rows depends on fr only
+  const int sw_w = swz<WB>(fr), sw_x = swz<XB>(fr);
   int w_off[FW], s_off[FW];
   #pragma unroll
   for (int f = 0; f < FW; ++f) {
     const int r = wn * WTW + f * 16 + fr;
-    w_off[f] = W_OFF + r * WB + ((fq ^ swz_w(r)) << 4);
+    w_off[f] = W_OFF + r * WB;
     s_off[f] = S_OFF + fq * WROWS + r;
   }
-  // gathered codes: row fi(i)*16 + fr, chunks fq and 4 + fq
+  // gathered codes, k-step kk: row fi(i)*16 + fr, chunks 8kk + fq and 8kk + 4 + fq
   auto fi = [&](int i) { return wm + WM * i; };
-  int x_off0[FMW], x_off1[FMW];
+  int x_off[FMW];
   #pragma unroll
-  for (int i = 0; i < FMW; ++i) {
-    const int r = fi(i) * 16 + fr;
-    x_off0[i] = r * XB + ((fq ^ swz_x(r)) << 4);
-    x_off1[i] = r * XB + (((4 + fq) ^ swz_x(r)) << 4);
-  }
+  for (int i = 0; i < FMW; ++i) x_off[i] = (fi(i) * 16 + fr) * XB;
 
   // 16-row fragments from ceil(valid / 16) on are all padding: skipped
   int fmv;
@@ -206,24 +213,27 @@ __global__ __launch_bounds__(WN * WM * kWave) void mx_up_kernel(Args g) {
     __syncthreads();
     issue(buf == 0 ? NS - 1 : buf - 1, min(kt + NS - 1, KT - 1));   // past the end: repeat, unread
     const char* stg = lds + buf * STAGE;
-    i32x8 wf[FW];
-    int sc[FW];
     #pragma unroll
-    for (int f = 0; f < FW; ++f) {
-      const i32x4 v = *reinterpret_cast<const i32x4*>(stg + w_off[f]);
-      wf[f] = i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-      sc[f] = *reinterpret_cast<const uint8_t*>(stg + s_off[f]);
-    }
-    #pragma unroll
-    for (int i = 0; i < FMW; ++i) {
-      if (fi(i) >= fmv) break;
-      const i32x4 lo = *reinterpret_cast<const i32x4*>(stg + x_off0[i]);
-      const i32x4 hi = *reinterpret_cast<const i32x4*>(stg + x_off1[i]);
-      const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    for (int kk = 0; kk < KSL; ++kk) {
+      i32x8 wf[FW];
+      int sc[FW];
       #pragma unroll
-      for (int f = 0; f < FW; ++f)
-        acc[f][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[f], xf, acc[f][i], 4, 0, 0,
-                                                                     sc[f], 0, 127);
+      for (int f = 0; f < FW; ++f) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(stg + w_off[f] + (((4 * kk + fq) ^ sw_w) << 4));
+        wf[f] = i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+        sc[f] = *reinterpret_cast<const uint8_t*>(stg + s_off[f] + 4 * kk * WROWS);
+      }
+      #pragma unroll
+      for (int i = 0; i < FMW; ++i) {
+        if (fi(i) >= fmv) break;
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(stg + x_off[i] + (((8 * kk + fq) ^ sw_x) << 4));
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(stg + x_off[i] + (((8 * kk + 4 + fq) ^ sw_x) << 4));
+        const i32x8 xf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        #pragma unroll
+        for (int f = 0; f < FW; ++f)
+          acc[f][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[f], xf, acc[f][i], 4, 0,
+                                                                       0, sc[f], 0, 127);
+      }
     }
     buf = (buf + 1 == NS) ? 0 : buf + 1;
   }
@@ -259,11 +269,12 @@ __global__ __launch_bounds__(WN * WM * kWave) void mx_up_kernel(Args g) {
   }
 }
 
-template <int BM, int BNA, int NS, int WM>
+template <int BM, int BNA, int NS, int WM, int KSL>
 hipError_t run(const Args& a, int64_t tiles_max, hipStream_t s) {
+  if (a.I % BNA) return hipErrorInvalidValue;
   const int64_t grid = (tiles_max * (a.I / BNA) + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((mx_up_kernel<BM, BNA, NS, WM>), dim3((unsigned)grid), dim3(WN * WM * kWave),
+  hipLaunchKernelGGL((mx_up_kernel<BM, BNA, NS, WM, KSL>), dim3((unsigned)grid), dim3(WN * WM * kWave),
                      0, s, a);
   return hipGetLastError();
 }
@@ -294,11 +305,18 @@ hipError_t launch_up_mxfp4(const Resolved& r, const uint8_t* x, const float* x_s
   a.I = r.I;
   a.top_k = r.K;
   a.n_slots = (int)r.N;
+  // Small m-blocks stream weights: narrow tiles keep two workgroups per CU and many
+  // workgroups in flight.  Large m-blocks are MFMA-bound: 384 weight rows per tile (96 per
+  // wave) read each gathered-row fragment for six MFMAs (GPT-OSS shard at 31744 tokens:
+  // 968 -> 1340 TFLOP/s against 128-row tiles; deeper rings or 256-value slices measured slower).
+  const bool wide = r.I % 192 == 0;
   switch (r.BM) {
-    case 16: return mx::run<16, 64, 6, 1>(a, r.tiles_max, s);
-    case 32: return mx::run<32, 64, 6, 1>(a, r.tiles_max, s);
-    case 64: return mx::run<64, 64, 5, 2>(a, r.tiles_max, s);
-    default: return mx::run<128, 64, 4, 2>(a, r.tiles_max, s);
+    case 16: return mx::run<16, 64, 6, 1, 1>(a, r.tiles_max, s);
+    case 32: return mx::run<32, 64, 6, 1, 1>(a, r.tiles_max, s);
+    case 64: return wide ? mx::run<64, 192, 4, 2, 1>(a, r.tiles_max, s)
+                         : mx::run<64, 64, 5, 2, 1>(a, r.tiles_max, s);
+    default: return wide ? mx::run<128, 192, 3, 2, 1>(a, r.tiles_max, s)
+                         : mx::run<128, 64, 4, 2, 1>(a, r.tiles_max, s);
   }
 }
 
