@@ -154,6 +154,19 @@ def dense_reference(args):
               flush=True)
 
 
+def warm_up(step, n, min_seconds=0.1):
+    """At least n untimed steps and at least min_seconds of GPU work: between sweep points the
+    host prepares the next routing and the GPU idles, and its clock needs the time to ramp."""
+    import torch
+    t0 = time.perf_counter()
+    k = 0
+    while k < n or time.perf_counter() - t0 < min_seconds:
+        step()
+        k += 1
+        if k % 8 == 0:
+            torch.cuda.synchronize()
+
+
 def sweep(args):
     """The 48-point batch sweep of one expert-parallel shard ("MOE Bmm1 Fused Gather", its bench:
     batch sizes and production-like routing).  Per batch size: the whole layer (align, up, down,
@@ -217,8 +230,7 @@ def sweep(args):
                 if ev: ev[3].record()
                 moe.moe_combine(p, slot_out, a["slot_row"], out)
                 if ev: ev[4].record()
-            for _ in range(args.warmup):
-                step()
+            warm_up(step, args.warmup)
             evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
             torch.cuda.synchronize()
             for k in range(args.steps):
@@ -331,8 +343,7 @@ def sweep_mx(args, base):
                                               case.alpha, case.limit, case.out_scale, a["sorted_slots"],
                                               a["offsets"], a["tiles"], a["num_tiles"], act)
                 if ev: ev[2].record()
-            for _ in range(args.warmup):
-                step()
+            warm_up(step, args.warmup)
             evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
             torch.cuda.synchronize()
             for k in range(args.steps):

@@ -305,18 +305,15 @@ hipError_t launch_up_mxfp4(const Resolved& r, const uint8_t* x, const float* x_s
   a.I = r.I;
   a.top_k = r.K;
   a.n_slots = (int)r.N;
-  // Small m-blocks stream weights: narrow tiles keep two workgroups per CU and many
-  // workgroups in flight.  Large m-blocks are MFMA-bound: 384 weight rows per tile (96 per
-  // wave) read each gathered-row fragment for six MFMAs (GPT-OSS shard at 31744 tokens:
-  // 968 -> 1340 TFLOP/s against 128-row tiles; deeper rings or 256-value slices measured slower).
-  const bool wide = r.I % 192 == 0;
+  // Three-stage rings of 128-row weight tiles for every block size: occupancy wins here.
+  // Measured on the GPT-OSS shard: two to five workgroups per CU beat deeper rings (6 stages:
+  // 25% slower at 640 tokens), 256-value slices, and 384-row weight tiles with one workgroup
+  // per CU (5-17% slower at 2048-31744 tokens).
   switch (r.BM) {
-    case 16: return mx::run<16, 64, 6, 1, 1>(a, r.tiles_max, s);
-    case 32: return mx::run<32, 64, 6, 1, 1>(a, r.tiles_max, s);
-    case 64: return wide ? mx::run<64, 192, 4, 2, 1>(a, r.tiles_max, s)
-                         : mx::run<64, 64, 5, 2, 1>(a, r.tiles_max, s);
-    default: return wide ? mx::run<128, 192, 3, 2, 1>(a, r.tiles_max, s)
-                         : mx::run<128, 64, 4, 2, 1>(a, r.tiles_max, s);
+    case 16: return mx::run<16, 64, 3, 1, 1>(a, r.tiles_max, s);
+    case 32: return mx::run<32, 64, 3, 1, 1>(a, r.tiles_max, s);
+    case 64: return mx::run<64, 64, 3, 2, 1>(a, r.tiles_max, s);
+    default: return mx::run<128, 64, 3, 2, 1>(a, r.tiles_max, s);
   }
 }
 
