@@ -449,9 +449,11 @@ hipError_t launch_up_stream(const Resolved& r, const void* x, const float* x_sca
   }
   if (r.I % 128 != 0) {   // I a multiple of 64 only: 64-wide n-blocks
     switch (r.BM) {
-      case 16: return st::run<OpBf16, 16, 64, 6, true, OUT_BF16>(a, s);
-      case 32: return st::run<OpBf16, 32, 64, 6, true, OUT_BF16>(a, s);
-      default: return st::run<OpBf16, 64, 64, 5, true, OUT_BF16>(a, s);
+      // shallow rings: more workgroups per CU (shard at 1024 tokens: down 0.103 -> 0.070 ms
+      // against 5-8 stages)
+      case 16: return st::run<OpBf16, 16, 64, 4, true, OUT_BF16>(a, s);
+      case 32: return st::run<OpBf16, 32, 64, 4, true, OUT_BF16>(a, s);
+      default: return st::run<OpBf16, 64, 64, 3, true, OUT_BF16>(a, s);
     }
   }
   switch (r.BM) {
@@ -506,9 +508,9 @@ hipError_t launch_down_stream(const Resolved& r, const void* act, const float* a
   }
   if (r.H % 128 != 0) {   // H a multiple of 64 only: 64-wide n-blocks
     switch (r.BM) {
-      case 16: return st::run<OpBf16, 16, 64, 8, false, OUT_BF16>(a, s);
-      case 32: return st::run<OpBf16, 32, 64, 8, false, OUT_BF16>(a, s);
-      default: return st::run<OpBf16, 64, 64, 6, false, OUT_BF16>(a, s);
+      case 16: return st::run<OpBf16, 16, 64, 4, false, OUT_BF16>(a, s);
+      case 32: return st::run<OpBf16, 32, 64, 4, false, OUT_BF16>(a, s);
+      default: return st::run<OpBf16, 64, 64, 3, false, OUT_BF16>(a, s);
     }
   }
   switch (r.BM) {   // H is a multiple of 128 only
