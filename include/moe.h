@@ -45,8 +45,17 @@ typedef enum moe_status {
   MOE_ERR_DTYPE = -3,      /* unsupported dtype or dtype combination                     */
   MOE_ERR_WORKSPACE = -4,  /* workspace smaller than moe_workspace_bytes()               */
   MOE_ERR_LAUNCH = -5,     /* a kernel launch failed (hipGetLastError after the launch)  */
-  MOE_ERR_DEVICE = -6      /* no usable device / not a gfx950 device                    */
+  MOE_ERR_DEVICE = -6,     /* no usable device / not a gfx950 device                    */
+  MOE_ERR_ALIGN = -7       /* a device pointer is not aligned as its argument requires  */
 } moe_status;
+
+/*
+ * Pointer alignment (checked on the host before any launch; MOE_ERR_ALIGN otherwise):
+ *   16 bytes: data arrays -- X and its codes, weights, act, slot rows, out, bias;
+ *   4 bytes:  int32 and fp32 index, routing-weight, logit and scale arrays;
+ *   256 bytes: moe_forward's workspace.
+ * Memory from hipMalloc or a torch allocation at offset 0 satisfies all of them.
+ */
 
 typedef enum moe_dtype {
   MOE_F32 = 0,   /* IEEE binary32                                                   */

@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     MOE_BF16,
     MOE_E4M3,
+    MOE_ERR_ALIGN,
     MOE_ERR_DEVICE,
     MOE_ERR_DTYPE,
     MOE_ERR_LAUNCH,

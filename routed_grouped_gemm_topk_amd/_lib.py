@@ -24,6 +24,7 @@ MOE_ERR_DTYPE = -3
 MOE_ERR_WORKSPACE = -4
 MOE_ERR_LAUNCH = -5
 MOE_ERR_DEVICE = -6
+MOE_ERR_ALIGN = -7
 
 MOE_F32, MOE_BF16, MOE_E4M3, MOE_MXFP4 = 0, 1, 2, 3
 _DT_NAME = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_E4M3, "mxfp4": MOE_MXFP4}

@@ -3,6 +3,7 @@
 // a rejected call enqueues nothing.
 #include <string.h>
 
+#include <initializer_list>
 #include <mutex>
 
 #include "moe_internal.h"
@@ -131,6 +132,17 @@ int check_device() {
 
 int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
 
+// MOE_ERR_ALIGN unless every non-null pointer is aligned to its byte count.
+struct Al {
+  const void* p;
+  int a;
+};
+int check_align(std::initializer_list<Al> ptrs) {
+  for (const Al& x : ptrs)
+    if (x.p && ((uintptr_t)x.p & (uintptr_t)(x.a - 1))) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -144,6 +156,7 @@ const char* moe_status_str(int status) {
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
     case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH: kernel launch failed";
     case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE: no gfx950 device current";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: a device pointer is not aligned as required";
     default: return "unknown moe_status";
   }
 }
@@ -187,6 +200,7 @@ int moe_route(const moe_problem* p, const float* logits, int renormalize, int32_
   if (v) return v;
   if (p->top_k > kRouteMaxK) return MOE_ERR_SHAPE;
   if (!logits || !topk_ids || !topk_weights) return MOE_ERR_NULL;
+  if ((v = check_align({{logits, 4}, {topk_ids, 4}, {topk_weights, 4}}))) return v;
   if ((v = check_device())) return v;
   const Resolved r = resolve(p);
   return status_of(launch_route(r, logits, renormalize, topk_ids, topk_weights, (hipStream_t)stream));
@@ -202,6 +216,10 @@ int moe_route_align(const moe_problem* p, const float* logits, int renormalize, 
   if (!logits || !topk_ids || !topk_weights || !counts || !offsets || !sorted_slots ||
       !slot_row || !tiles || !num_tiles || !n_invalid)
     return MOE_ERR_NULL;
+  if ((v = check_align({{logits, 4}, {topk_ids, 4}, {topk_weights, 4}, {counts, 4}, {offsets, 4},
+                        {sorted_slots, 4}, {slot_row, 4}, {tiles, 4}, {num_tiles, 4},
+                        {n_invalid, 4}})))
+    return v;
   if ((v = check_device())) return v;
   const Resolved r = resolve(p);
   return status_of(launch_route_align(r, logits, renormalize, topk_ids, topk_weights, counts,
@@ -217,6 +235,9 @@ int moe_align(const moe_problem* p, const int32_t* topk_ids, int32_t* counts, in
   if (!topk_ids || !counts || !offsets || !sorted_slots || !slot_row || !tiles || !num_tiles ||
       !n_invalid)
     return MOE_ERR_NULL;
+  if ((v = check_align({{topk_ids, 4}, {counts, 4}, {offsets, 4}, {sorted_slots, 4},
+                        {slot_row, 4}, {tiles, 4}, {num_tiles, 4}, {n_invalid, 4}})))
+    return v;
   if ((v = check_device())) return v;
   const Resolved r = resolve(p);
   return status_of(launch_align(r, topk_ids, counts, offsets, sorted_slots, slot_row, tiles,
@@ -229,6 +250,7 @@ int moe_quantize_rows_e4m3(const moe_problem* p, const void* x, uint8_t* xq, flo
   if (v) return v;
   if (p->w_dtype != MOE_E4M3 || p->dtype != MOE_BF16) return MOE_ERR_DTYPE;
   if (!x || !xq || !scales) return MOE_ERR_NULL;
+  if ((v = check_align({{x, 16}, {xq, 16}, {scales, 4}}))) return v;
   if ((v = check_device())) return v;
   return status_of(launch_quant_rows(resolve(p), x, xq, scales, (hipStream_t)stream));
 }
@@ -242,6 +264,9 @@ int moe_grouped_gemm_up(const moe_problem* p, const void* x, const float* x_scal
   if (is_mx(p)) return MOE_ERR_DTYPE;
   if (!x || !w13 || !sorted_slots || !offsets || !tiles || !num_tiles || !act) return MOE_ERR_NULL;
   if (p->w_dtype == MOE_E4M3 && (!x_scales || !w13_scales || !act_scales)) return MOE_ERR_NULL;
+  if ((v = check_align({{x, 16}, {x_scales, 4}, {w13, 16}, {w13_scales, 4}, {sorted_slots, 4},
+                        {offsets, 4}, {tiles, 4}, {num_tiles, 4}, {act, 16}, {act_scales, 4}})))
+    return v;
   if ((v = check_device())) return v;
   return status_of(launch_up(resolve(p), x, x_scales, w13, w13_scales, sorted_slots, offsets,
                              tiles, num_tiles, act, act_scales, (hipStream_t)stream));
@@ -259,6 +284,10 @@ int moe_grouped_gemm_up_mxfp4(const moe_problem* p, const uint8_t* x, const floa
   if (!x || !x_scale || !w13 || !w13_scales || !bias || !out_scale || !sorted_slots ||
       !offsets || !tiles || !num_tiles || !act)
     return MOE_ERR_NULL;
+  if ((v = check_align({{x, 16}, {x_scale, 4}, {w13, 16}, {w13_scales, 4}, {bias, 16},
+                        {out_scale, 4}, {sorted_slots, 4}, {offsets, 4}, {tiles, 4},
+                        {num_tiles, 4}, {act, 16}})))
+    return v;
   if ((v = check_device())) return v;
   return status_of(launch_up_mxfp4(resolve(p), x, x_scale, w13, w13_scales, bias, alpha, limit,
                                    out_scale, sorted_slots, offsets, tiles, num_tiles, act,
@@ -277,6 +306,10 @@ int moe_grouped_gemm_down(const moe_problem* p, const void* act, const float* ac
       !slot_out)
     return MOE_ERR_NULL;
   if (p->w_dtype == MOE_E4M3 && (!act_scales || !w2_scales)) return MOE_ERR_NULL;
+  if ((v = check_align({{act, 16}, {act_scales, 4}, {w2, 16}, {w2_scales, 4}, {topk_weights, 4},
+                        {sorted_slots, 4}, {offsets, 4}, {tiles, 4}, {num_tiles, 4},
+                        {slot_out, 16}})))
+    return v;
   if ((v = check_device())) return v;
   return status_of(launch_down(resolve(p), act, act_scales, w2, w2_scales, topk_weights,
                                sorted_slots, offsets, tiles, num_tiles, slot_out,
@@ -289,6 +322,7 @@ int moe_combine(const moe_problem* p, const void* slot_out, const int32_t* slot_
   if (v) return v;
   if (is_mx(p)) return MOE_ERR_DTYPE;
   if (!slot_out || !slot_row || !out) return MOE_ERR_NULL;
+  if ((v = check_align({{slot_out, 16}, {slot_row, 4}, {out, 16}}))) return v;
   if ((v = check_device())) return v;
   return status_of(launch_combine(resolve(p), slot_out, slot_row, out, (hipStream_t)stream));
 }
@@ -306,6 +340,9 @@ int moe_forward(const moe_problem* p, const void* x, const int32_t* topk_ids,
   const Resolved r = resolve(p);
   const Layout L = layout(r);
   if ((int64_t)workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if ((v = check_align({{x, 16}, {topk_ids, 4}, {topk_weights, 4}, {w13, 16}, {w13_scales, 4},
+                        {w2, 16}, {w2_scales, 4}, {out, 16}, {workspace, 256}})))
+    return v;
   if ((v = check_device())) return v;
 
   char* ws = (char*)workspace;

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(-6, 1):
+    for code in range(-7, 1):
         assert moe.status_str(code).startswith("MOE_")
     assert "unknown" in moe.status_str(-99)
 
@@ -185,3 +185,32 @@ def test_mxfp4_problem_validation(lib):
     assert lib.moe_grouped_gemm_up_mxfp4(bf, *mxargs, None) == moe.MOE_ERR_DTYPE
     nulls = [None] * 5 + [ctypes.c_float(1.1), ctypes.c_float(1.4)] + [None] * 6
     assert lib.moe_grouped_gemm_up_mxfp4(P, *nulls, None) == moe.MOE_ERR_NULL
+
+
+def test_misaligned_pointers_are_rejected_before_any_launch(lib):
+    """Data arrays need 16-byte alignment, index/scale arrays 4, the workspace 256; a
+    misaligned pointer returns MOE_ERR_ALIGN on the host (no device is touched)."""
+    p = bad(T=16, H=128, I=256, E=8, top_k=2)
+    P = ctypes.byref(p)
+    ok, odd8, odd2 = ctypes.c_void_p(4096), ctypes.c_void_p(4096 + 8), ctypes.c_void_p(4096 + 2)
+    A = moe.MOE_ERR_ALIGN
+    assert lib.moe_align(P, odd2, *[ok] * 7, None) == A
+    assert lib.moe_align(P, ok, ok, ok, ok, ok, ok, ok, odd2, None) == A
+    assert lib.moe_route(P, odd2, 0, ok, ok, None) == A
+    assert lib.moe_route_align(P, ok, 0, ok, ok, ok, ok, ok, ok, odd2, ok, ok, None) == A
+    assert lib.moe_grouped_gemm_up(P, odd8, None, ok, None, ok, ok, ok, ok, ok, None, None) == A
+    assert lib.moe_grouped_gemm_up(P, ok, None, ok, None, ok, ok, ok, ok, odd8, None, None) == A
+    assert lib.moe_grouped_gemm_down(P, ok, None, odd8, None, ok, ok, ok, ok, ok, ok, None) == A
+    assert lib.moe_grouped_gemm_down(P, ok, None, ok, None, odd2, ok, ok, ok, ok, ok, None) == A
+    assert lib.moe_combine(P, ok, ok, odd8, None) == A
+    need = moe.moe_workspace_bytes(p)
+    assert lib.moe_forward(P, ok, ok, ok, ok, None, ok, None, ok, ctypes.c_void_p(4096 + 128),
+                           need, None) == A
+    assert lib.moe_forward(P, ok, ok, odd2, ok, None, ok, None, ok, ok, need, None) == A
+    pf = bad(w_dtype="e4m3")
+    assert lib.moe_quantize_rows_e4m3(ctypes.byref(pf), odd8, ok, ok, None) == A
+    mxp = ctypes.byref(moe.make_problem(16, 192, 128, 8, 2, "e4m3", "mxfp4"))
+    args = [ok, ok, ok, ok, odd8, ctypes.c_float(1.1), ctypes.c_float(1.4), ok, ok, ok, ok, ok, ok]
+    assert lib.moe_grouped_gemm_up_mxfp4(mxp, *args, None) == A           # bias
+    args[4], args[-1] = ok, odd8
+    assert lib.moe_grouped_gemm_up_mxfp4(mxp, *args, None) == A           # act
