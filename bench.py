@@ -399,6 +399,8 @@ def main():
     ap.add_argument("--routing", choices=["on", "off"], default="off",
                     help="on: the step starts from router logits (moe_route_align replaces "
                          "moe_align and produces the ids and weights the GEMMs use)")
+    ap.add_argument("--graph", choices=["on", "off"], default="on",
+                    help="also time the step replayed from a HIP graph (ms_per_step_graph)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (to scale FETCH_SIZE/WRITE_SIZE)")
     ap.add_argument("--dense-reference", action="store_true",
@@ -516,6 +518,28 @@ def main():
                for i, s in enumerate(stages)}
     log(f"staged step {ms_per_step:.4f} ms; kernels " + ", ".join(f"{k} {v:.4f}" for k, v in kern_ms.items()))
 
+    # the same step captured once in a HIP graph and replayed (launch overhead removed)
+    ms_graph = None
+    if args.graph == "on":
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        tg = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms_graph = (time.perf_counter() - tg) * 1e3 / args.steps
+        log(f"graph-replayed step {ms_graph:.4f} ms")
+        del graph
+
     # moe_forward on its own (one entry point, same kernels)
     for _ in range(3):
         moe.forward(p, case.x, case.topk_ids, case.topk_weights, case.w13, case.w2, case.w13_scales,
@@ -605,6 +629,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "ms_per_step_forward": round(ms_forward, 5),
+        "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
