@@ -457,7 +457,9 @@ hipError_t launch_up_stream(const Resolved& r, const void* x, const float* x_sca
     }
   }
   switch (r.BM) {
-    case 16: return st::run<OpBf16, 16, 128, 4, true, OUT_BF16>(a, s);
+    // 16-row blocks (decode): 64-wide n-blocks, twice the workgroups (DeepSeek-V3 decode up
+    // 2.033 -> 2.001 ms against 128-wide)
+    case 16: return st::run<OpBf16, 16, 64, 6, true, OUT_BF16>(a, s);
     case 32: return st::run<OpBf16, 32, 128, 4, true, OUT_BF16>(a, s);
     default: return st::run<OpBf16, 64, 128, 3, true, OUT_BF16>(a, s);
   }
@@ -501,7 +503,9 @@ hipError_t launch_down_stream(const Resolved& r, const void* act, const float* a
   }
   if (r.H % 256 == 0) {
     switch (r.BM) {
-      case 16: return st::run<OpBf16, 16, 256, 4, false, OUT_BF16>(a, s);
+      // 16-row blocks: 128-wide n-blocks and 3 stages, two workgroups per CU (decode down
+      // with K = 2048: 1.063 -> 0.999 ms against 256-wide, 4 stages)
+      case 16: return st::run<OpBf16, 16, 128, 3, false, OUT_BF16>(a, s);
       case 32: return st::run<OpBf16, 32, 256, 4, false, OUT_BF16>(a, s);
       default: return st::run<OpBf16, 64, 256, 3, false, OUT_BF16>(a, s);
     }
