@@ -154,6 +154,20 @@ def dense_reference(args):
               flush=True)
 
 
+def write_sweep_table(args, base, device_name, columns, rows, note=""):
+    """Markdown table of a batch sweep: `columns` is a list of (header, JSON key) pairs."""
+    with open(args.sweep_out, "w") as f:
+        f.write(f"# Batch sweep: {base.name}\n\n{base.description}.\n\n")
+        f.write("Command: `python bench.py " + " ".join(sys.argv[1:]) + "`\n\n")
+        f.write(f"Device: {device_name}; kernel_source_sha256 `{kernel_source_digest()}`; times are "
+                f"HIP-event means over {args.steps} steps after at least {args.warmup} warm-up "
+                f"steps and 100 ms.{note}\n\n")
+        f.write("| " + " | ".join(h for h, _ in columns) + " |\n|" + "---|" * len(columns) + "\n")
+        for r in rows:
+            f.write("| " + " | ".join(str(r.get(k)) for _, k in columns) + " |\n")
+    log(f"wrote {args.sweep_out}")
+
+
 def warm_up(step, n, min_seconds=0.1):
     """At least n untimed steps and at least min_seconds of GPU work: between sweep points the
     host prepares the next routing and the GPU idles, and its clock needs the time to ramp."""
@@ -273,25 +287,14 @@ def sweep(args):
         del ids, wts
         torch.cuda.empty_cache()
     if args.sweep_out:
-        with open(args.sweep_out, "w") as f:
-            f.write(f"# Batch sweep: {base.name}\n\n{base.description}.\n\n")
-            f.write("Command: `python bench.py " + " ".join(sys.argv[1:]) + "`\n\n")
-            f.write(f"Device: {torch.cuda.get_device_name(dev)}; kernel_source_sha256 "
-                    f"`{kernel_source_digest()}`; times are HIP-event means over {args.steps} steps "
-                    f"after {args.warmup} warmup steps.\n\n")
-            hdr = ["T", "tok/exp", "local slots", "max/exp", "bm", "up ms", "up TF/s", "up % peak",
-                   "up roofline frac", "layer ms", "layer TF/s"]
-            if cands:
-                hdr += ["best bm", "best layer ms"]
-            f.write("| " + " | ".join(hdr) + " |\n|" + "---|" * len(hdr) + "\n")
-            for r in rows_md:
-                v = [r["T"], r["tokens_per_expert"], r["local_slots"], r["max_per_expert"], r["block_m"],
-                     r["up_ms"], r["up_TFLOP/s"], r["up_pct_mfma_peak"], r["up_roofline_frac"],
-                     r["layer_ms"], r["layer_TFLOP/s"]]
-                if cands:
-                    v += [r.get("best_block_m"), r.get("best_layer_ms")]
-                f.write("| " + " | ".join(str(c) for c in v) + " |\n")
-        log(f"wrote {args.sweep_out}")
+        cols = [("T", "T"), ("tok/exp", "tokens_per_expert"), ("local slots", "local_slots"),
+                ("max/exp", "max_per_expert"), ("bm", "block_m"), ("up ms", "up_ms"),
+                ("up TF/s", "up_TFLOP/s"), ("up % peak", "up_pct_mfma_peak"),
+                ("up roofline frac", "up_roofline_frac"), ("layer ms", "layer_ms"),
+                ("layer TF/s", "layer_TFLOP/s")]
+        if cands:
+            cols += [("best bm", "best_block_m"), ("best layer ms", "best_layer_ms")]
+        write_sweep_table(args, base, torch.cuda.get_device_name(dev), cols, rows_md)
 
 
 def sweep_mx(args, base):
@@ -369,23 +372,14 @@ def sweep_mx(args, base):
         rows_md.append(pt)
         del ids
     if args.sweep_out:
-        with open(args.sweep_out, "w") as f:
-            f.write(f"# Batch sweep: {base.name}\n\n{base.description}.\n\n")
-            f.write("Command: `python bench.py " + " ".join(sys.argv[1:]) + "`\n\n")
-            f.write(f"Device: {torch.cuda.get_device_name(dev)}; kernel_source_sha256 "
-                    f"`{kernel_source_digest()}`; times are HIP-event means over {args.steps} steps "
-                    f"after {args.warmup} warmup steps.  Peak: {peak_tf} TFLOP/s (fp8 MFMA), "
-                    f"{PEAK_HBM_GBS / 1000} TB/s.\n\n")
-            hdr = ["T", "tok/exp", "local slots", "max/exp", "bm", "up ms", "TFLOP/s", "% fp8 peak",
-                   "TB/s", "roofline frac"] + (["best bm", "best ms"] if cands else [])
-            f.write("| " + " | ".join(hdr) + " |\n|" + "---|" * len(hdr) + "\n")
-            for r in rows_md:
-                v = [r["T"], r["tokens_per_expert"], r["local_slots"], r["max_per_expert"], r["block_m"],
-                     r["up_ms"], r["up_TFLOP/s"], r["up_pct_fp8_peak"], r["up_TB/s"], r["up_roofline_frac"]]
-                if cands:
-                    v += [r.get("best_block_m"), r.get("best_up_ms")]
-                f.write("| " + " | ".join(str(c) for c in v) + " |\n")
-        log(f"wrote {args.sweep_out}")
+        cols = [("T", "T"), ("tok/exp", "tokens_per_expert"), ("local slots", "local_slots"),
+                ("max/exp", "max_per_expert"), ("bm", "block_m"), ("up ms", "up_ms"),
+                ("TFLOP/s", "up_TFLOP/s"), ("% fp8 peak", "up_pct_fp8_peak"), ("TB/s", "up_TB/s"),
+                ("roofline frac", "up_roofline_frac")]
+        if cands:
+            cols += [("best bm", "best_block_m"), ("best ms", "best_up_ms")]
+        write_sweep_table(args, base, torch.cuda.get_device_name(dev), cols, rows_md,
+                          note=f"  Peak: {peak_tf} TFLOP/s (fp8 MFMA), {PEAK_HBM_GBS / 1000} TB/s.")
 
 
 def main():
