@@ -99,6 +99,10 @@ SWEEP_CONFIGS = {
                   x_dtype="e4m3", renormalize=True, route_experts=128, prod_like=True,
                   description="the same shard's first expert GEMM as the page runs it: MXFP4 "
                               "weights x e4m3 activations, bias, GPT-OSS SwiGLU, e4m3 output"),
+        MoEConfig("gptoss_shard_uniform_mxfp4", T=31744, H=2880, I=2880, E=16, top_k=4,
+                  w_dtype="mxfp4", x_dtype="e4m3", renormalize=True, route_experts=128,
+                  description="the MXFP4 first expert GEMM of the shard with logits ~N(0,1) "
+                              "(the bench's uniform routing)"),
         MoEConfig("gptoss_shard_uniform_bf16", T=31744, H=2880, I=2880, E=16, top_k=4,
                   w_dtype="bf16", x_dtype="bf16", renormalize=True, route_experts=128,
                   description="the same shard with logits ~N(0,1) (the bench's uniform routing)"),
