@@ -230,6 +230,7 @@ def sweep(args):
             act = torch.empty((moe.moe_max_padded_slots(p), I), dtype=torch.bfloat16, device=dev)
             slot_out = torch.empty((T * K, H), dtype=torch.bfloat16, device=dev)
             out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            dws = moe.alloc_down_workspace(p, dev)
 
             def step(ev=None):
                 if ev: ev[0].record()
@@ -240,7 +241,7 @@ def sweep(args):
                                         a["tiles"], a["num_tiles"], act, None)
                 if ev: ev[2].record()
                 moe.moe_grouped_gemm_down(p, act, None, case.w2, None, wts, a["sorted_slots"],
-                                          a["offsets"], a["tiles"], a["num_tiles"], slot_out)
+                                          a["offsets"], a["tiles"], a["num_tiles"], slot_out, dws)
                 if ev: ev[3].record()
                 moe.moe_combine(p, slot_out, a["slot_row"], out)
                 if ev: ev[4].record()
@@ -455,6 +456,7 @@ def main():
     slot_out = torch.empty((cfg.T * cfg.top_k, cfg.H), dtype=case.x.dtype, device=dev)
     out = torch.empty((cfg.T, cfg.H), dtype=case.x.dtype, device=dev)
     ws = moe.alloc_workspace(p, dev)
+    down_ws = moe.alloc_down_workspace(p, dev)
     routing = args.routing == "on"
     if routing:
         from moe_inputs import make_logits
@@ -490,7 +492,8 @@ def main():
         mark()
         moe.moe_grouped_gemm_down(p, act, act_scales, case.w2, case.w2_scales,
                                   r_w if routing else case.topk_weights,
-                                  a["sorted_slots"], a["offsets"], a["tiles"], a["num_tiles"], slot_out)
+                                  a["sorted_slots"], a["offsets"], a["tiles"], a["num_tiles"], slot_out,
+                                  down_ws)
         mark()
         moe.moe_combine(p, slot_out, a["slot_row"], out)
         mark()

@@ -53,7 +53,7 @@ typedef enum moe_status {
  * Pointer alignment (checked on the host before any launch; MOE_ERR_ALIGN otherwise):
  *   16 bytes: data arrays -- X and its codes, weights, act, slot rows, out, bias;
  *   4 bytes:  int32 and fp32 index, routing-weight, logit and scale arrays;
- *   256 bytes: moe_forward's workspace.
+ *   256 bytes: the workspaces of moe_forward and moe_grouped_gemm_down.
  * Memory from hipMalloc or a torch allocation at offset 0 satisfies all of them.
  */
 
@@ -251,12 +251,23 @@ int moe_grouped_gemm_up_mxfp4(const moe_problem* p, const uint8_t* x, const floa
  *      sorted_slots, offsets, tiles, num_tiles: outputs of moe_align for the same problem
  * Out: slot_out dtype [N, H] (bf16 for E4M3 weights).  Rows of excluded slots
  *      are not written.
+ * workspace: NULL, or device memory of at least moe_down_workspace_bytes(p) bytes,
+ *      256-byte aligned (MOE_ERR_WORKSPACE if smaller, MOE_ERR_ALIGN if misaligned);
+ *      caller-owned scratch whose contents are unspecified afterwards.  With it, bf16
+ *      problems of 128- or 256-row m-blocks cut the tiles of the GEMM's last, partly
+ *      filled round of workgroups along K into parts whose fp32 partial sums are added
+ *      in a fixed order: the result is deterministic, but its rounding differs from a
+ *      call without workspace.  Calls that share a workspace must not overlap.
  */
 int moe_grouped_gemm_down(const moe_problem* p, const void* act, const float* act_scales,
                           const void* w2, const float* w2_scales, const float* topk_weights,
                           const int32_t* sorted_slots, const int32_t* offsets,
                           const int32_t* tiles, const int32_t* num_tiles, void* slot_out,
-                          void* stream);
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the optional workspace of moe_grouped_gemm_down (0: the problem's down GEMM
+ * never uses one); negative moe_status for an invalid problem. */
+int64_t moe_down_workspace_bytes(const moe_problem* p);
 
 /*
  * moe_combine -- deterministic per-token combine, no atomics.

@@ -33,6 +33,7 @@ from ._lib import (  # noqa: F401
     moe_align,
     moe_block_m_for,
     moe_combine,
+    moe_down_workspace_bytes,
     moe_forward,
     moe_grouped_gemm_down,
     moe_grouped_gemm_up,
@@ -87,6 +88,12 @@ def route_align(p: Problem, logits: torch.Tensor, renormalize: bool, stream=None
 
 def alloc_workspace(p: Problem, device) -> torch.Tensor:
     return torch.empty(moe_workspace_bytes(p), dtype=torch.uint8, device=device)
+
+
+def alloc_down_workspace(p: Problem, device) -> Optional[torch.Tensor]:
+    """The optional workspace of moe_grouped_gemm_down (None when the problem needs none)."""
+    n = moe_down_workspace_bytes(p)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
 
 
 def forward(p: Problem, x, topk_ids, topk_weights, w13, w2, w13_scales=None, w2_scales=None,

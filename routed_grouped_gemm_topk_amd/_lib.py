@@ -33,7 +33,7 @@ _TORCH_DT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_E4M3: torch.f
 EXPORTS = ["moe_status_str", "moe_validate", "moe_pick_block_m", "moe_block_m_for", "moe_max_padded_slots",
            "moe_max_tiles", "moe_workspace_bytes", "moe_route", "moe_route_align", "moe_align",
            "moe_quantize_rows_e4m3", "moe_grouped_gemm_up", "moe_grouped_gemm_up_mxfp4",
-           "moe_grouped_gemm_down",
+           "moe_grouped_gemm_down", "moe_down_workspace_bytes",
            "moe_combine", "moe_forward"]
 
 
@@ -91,7 +91,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "moe_grouped_gemm_up": (ctypes.c_int, [P] + [vp] * 10 + [vp]),
         "moe_grouped_gemm_up_mxfp4": (ctypes.c_int, [P] + [vp] * 5 + [ctypes.c_float] * 2
                                       + [vp] * 6 + [vp]),
-        "moe_grouped_gemm_down": (ctypes.c_int, [P] + [vp] * 10 + [vp]),
+        "moe_grouped_gemm_down": (ctypes.c_int, [P] + [vp] * 11 + [ctypes.c_size_t, vp]),
+        "moe_down_workspace_bytes": (ctypes.c_int64, [P]),
         "moe_combine": (ctypes.c_int, [P, vp, vp, vp, vp]),
         "moe_forward": (ctypes.c_int, [P] + [vp] * 9 + [ctypes.c_size_t, vp]),
     }
@@ -141,6 +142,10 @@ def moe_max_tiles(p: Problem) -> int:
 
 def moe_workspace_bytes(p: Problem) -> int:
     return _checked(load().moe_workspace_bytes(ctypes.byref(p)), "moe_workspace_bytes")
+
+
+def moe_down_workspace_bytes(p: Problem) -> int:
+    return _checked(load().moe_down_workspace_bytes(ctypes.byref(p)), "moe_down_workspace_bytes")
 
 
 # ---------------------------------------------------------------------------------------------
@@ -267,7 +272,7 @@ def moe_grouped_gemm_up_mxfp4(p: Problem, x, x_scale, w13, w13_scales, bias, alp
 
 
 def moe_grouped_gemm_down(p: Problem, act, act_scales, w2, w2_scales, topk_weights, sorted_slots,
-                          offsets, tiles, num_tiles, slot_out, stream=None) -> None:
+                          offsets, tiles, num_tiles, slot_out, workspace=None, stream=None) -> None:
     rows = moe_max_padded_slots(p)
     fp8 = p.w_dtype == MOE_E4M3
     args = [_ptr(act, "act", (_act_dtype(p), torch.float8_e4m3fn) if fp8 else _act_dtype(p), rows * p.I),
@@ -279,7 +284,9 @@ def moe_grouped_gemm_down(p: Problem, act, act_scales, w2, w2_scales, topk_weigh
             _ptr(offsets, "offsets", torch.int32, p.E + 1),
             _ptr(tiles, "tiles", torch.int32, 2 * moe_max_tiles(p)),
             _ptr(num_tiles, "num_tiles", torch.int32, 1),
-            _ptr(slot_out, "slot_out", _TORCH_DT[p.dtype], p.T * p.top_k * p.H)]
+            _ptr(slot_out, "slot_out", _TORCH_DT[p.dtype], p.T * p.top_k * p.H),
+            _ptr(workspace, "workspace", torch.uint8),
+            0 if workspace is None else workspace.numel() * workspace.element_size()]
     _checked(load().moe_grouped_gemm_down(ctypes.byref(p), *args, _stream(stream)),
              "moe_grouped_gemm_down")
 

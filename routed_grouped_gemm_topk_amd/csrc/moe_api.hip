@@ -91,7 +91,7 @@ Resolved resolve(const moe_problem* p) {
 // Workspace pieces of moe_forward, in order, each 256-byte aligned.
 struct Layout {
   int64_t status, counts, offsets, sorted_slots, slot_row, tiles, num_tiles;
-  int64_t xq, x_scales, act, act_scales, slot_out, total;
+  int64_t xq, x_scales, act, act_scales, slot_out, split, total;
 };
 
 Layout layout(const Resolved& r) {
@@ -111,23 +111,28 @@ Layout layout(const Resolved& r) {
   L.act = take(r.rows_max * r.I * (fp8 ? 1 : elt_bytes(r.dtype)));
   L.act_scales = fp8 ? take(4LL * r.rows_max * (r.I / kGroup)) : -1;
   L.slot_out = take(r.N * r.H * elt_bytes(r.dtype));
+  const int64_t split = down_split_bytes(r);
+  L.split = split > 0 ? take(split) : -1;
   L.total = o;
   return L;
 }
 
-// gfx950 check, cached per device ordinal.
+std::mutex g_dev_mu;
+int8_t g_dev_ok[64];      // 0 unknown, 1 ok, -1 not gfx950
+int g_dev_cus[64];        // compute units, 0 until known
+
+// gfx950 check, cached per device ordinal (with the device's compute-unit count).
 int check_device() {
-  static std::mutex mu;
-  static int8_t ok[64];   // 0 unknown, 1 ok, -1 not gfx950
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_DEVICE;
-  std::lock_guard<std::mutex> g(mu);
-  if (ok[dev] == 0) {
+  std::lock_guard<std::mutex> g(g_dev_mu);
+  if (g_dev_ok[dev] == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_DEVICE;
-    ok[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    g_dev_ok[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    g_dev_cus[dev] = prop.multiProcessorCount;
   }
-  return ok[dev] == 1 ? MOE_OK : MOE_ERR_DEVICE;
+  return g_dev_ok[dev] == 1 ? MOE_OK : MOE_ERR_DEVICE;
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
@@ -144,6 +149,15 @@ int check_align(std::initializer_list<Al> ptrs) {
 }
 
 }  // namespace
+
+// Every entry point runs check_device() before it launches, so the count is known here;
+// 0 (unknown) turns the down GEMM's K-split tail off.
+int moe::device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> g(g_dev_mu);
+  return g_dev_cus[dev];
+}
 
 extern "C" {
 
@@ -185,6 +199,13 @@ int64_t moe_max_padded_slots(const moe_problem* p) {
 int64_t moe_max_tiles(const moe_problem* p) {
   const int v = validate(p);
   return v != MOE_OK ? v : resolve(p).tiles_max;
+}
+
+int64_t moe_down_workspace_bytes(const moe_problem* p) {
+  const int v = validate(p);
+  if (v != MOE_OK) return v;
+  if (is_mx(p)) return MOE_ERR_DTYPE;
+  return down_split_bytes(resolve(p));
 }
 
 int64_t moe_workspace_bytes(const moe_problem* p) {
@@ -298,7 +319,7 @@ int moe_grouped_gemm_down(const moe_problem* p, const void* act, const float* ac
                           const void* w2, const float* w2_scales, const float* topk_weights,
                           const int32_t* sorted_slots, const int32_t* offsets,
                           const int32_t* tiles, const int32_t* num_tiles, void* slot_out,
-                          void* stream) {
+                          void* workspace, size_t workspace_bytes, void* stream) {
   int v = validate(p);
   if (v) return v;
   if (is_mx(p)) return MOE_ERR_DTYPE;
@@ -306,14 +327,17 @@ int moe_grouped_gemm_down(const moe_problem* p, const void* act, const float* ac
       !slot_out)
     return MOE_ERR_NULL;
   if (p->w_dtype == MOE_E4M3 && (!act_scales || !w2_scales)) return MOE_ERR_NULL;
+  const Resolved r = resolve(p);
+  const int64_t split = down_split_bytes(r);
+  if (workspace && (int64_t)workspace_bytes < split) return MOE_ERR_WORKSPACE;
   if ((v = check_align({{act, 16}, {act_scales, 4}, {w2, 16}, {w2_scales, 4}, {topk_weights, 4},
                         {sorted_slots, 4}, {offsets, 4}, {tiles, 4}, {num_tiles, 4},
-                        {slot_out, 16}})))
+                        {slot_out, 16}, {workspace, 256}})))
     return v;
   if ((v = check_device())) return v;
-  return status_of(launch_down(resolve(p), act, act_scales, w2, w2_scales, topk_weights,
-                               sorted_slots, offsets, tiles, num_tiles, slot_out,
-                               (hipStream_t)stream));
+  return status_of(launch_down(r, act, act_scales, w2, w2_scales, topk_weights, sorted_slots,
+                               offsets, tiles, num_tiles, slot_out,
+                               split > 0 ? workspace : nullptr, (hipStream_t)stream));
 }
 
 int moe_combine(const moe_problem* p, const void* slot_out, const int32_t* slot_row, void* out,
@@ -371,7 +395,7 @@ int moe_forward(const moe_problem* p, const void* x, const int32_t* topk_ids,
                 at(L.act), (float*)at(L.act_scales), s);
   if (e != hipSuccess) return MOE_ERR_LAUNCH;
   e = launch_down(r, at(L.act), (const float*)at(L.act_scales), w2, w2_scales, topk_weights,
-                  sorted_slots, offsets, tiles, num_tiles, at(L.slot_out), s);
+                  sorted_slots, offsets, tiles, num_tiles, at(L.slot_out), at(L.split), s);
   if (e != hipSuccess) return MOE_ERR_LAUNCH;
   e = launch_combine(r, at(L.slot_out), slot_row, out, s);
   return status_of(e);

@@ -411,10 +411,11 @@ hipError_t launch_up(const Resolved& r, const void* x, const float* x_scales, co
 hipError_t launch_down(const Resolved& r, const void* act, const float* act_scales,
                        const void* w2, const float* w2_scales, const float* topk_w,
                        const int32_t* sorted_slots, const int32_t* offsets, const int32_t* tiles,
-                       const int32_t* num_tiles, void* slot_out, hipStream_t s) {
+                       const int32_t* num_tiles, void* slot_out, void* split_ws,
+                       hipStream_t s) {
   if (prefill_supported(r))
     return launch_down_prefill(r, act, w2, topk_w, sorted_slots, offsets, tiles, num_tiles,
-                               slot_out, s);
+                               slot_out, split_ws, s);
   if (stream_supported(r))
     return launch_down_stream(r, act, act_scales, w2, w2_scales, topk_w, sorted_slots, offsets,
                               tiles, num_tiles, slot_out, s);

@@ -23,6 +23,7 @@
 //     that order is dealt to the XCDs (own L2 each) in chunks of 32 tiles, so concurrent
 //     workgroups of an XCD share rows and weights, and a hot expert's tiles spread over all
 //     XCDs (one contiguous range per XCD measured about 3% slower on large batches).
+#include <algorithm>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -55,9 +56,39 @@ struct Args {
   const int32_t* num_tiles;
   const float* topk_w;      // down
   uint16_t* out;            // up: act [rows_max, I]; down: slot_out [N, H]  (bf16 bits)
+  float* part;              // down: fp32 partial tiles of the K-split tail, or null
   int K, n_out, top_k, n_slots, tiles_max;
+  int slots;                // down with part: workgroup slots of the device (one per CU), else 0
+  int grid_tiles;           // blocks [0, grid_tiles) run whole tiles, the rest K-split units
   int64_t w_expert_elems;
 };
+
+// K-split of the last round (down GEMM).  The logical tiles run in rounds of `slots`
+// workgroups (one per CU); when the last round holds only r < slots tiles, those r tiles
+// are cut along K into S parts, S = min(slots / r, K slices / kMinSplitSlices, kMaxSplit),
+// so the last round is r*S short units instead of r whole tiles beside idle CUs.  Each unit
+// writes its fp32 partial tile; split_reduce_kernel adds the S partials of a row in
+// ascending part order (fixed, so the result does not depend on timing), applies the
+// routing weight and rounds once.
+constexpr int kSplitBK = 64;          // k-slice of every prefill launch that may split
+constexpr int kMinSplitSlices = 8;    // at least 512 of K per part
+constexpr int kMaxSplit = 16;
+constexpr int kMaxSplitUnits = 256;   // r*S <= slots <= this (sizes the partial buffer)
+
+struct TailSplit { int full, r, S; };
+
+__device__ __forceinline__ TailSplit tail_split(int total, int slots, int kt_all) {
+  TailSplit t{total, 0, 1};
+  if (slots <= 0) return t;
+  const int r = total % slots;
+  if (r == 0) return t;
+  const int S = min(min(slots / r, kt_all / kMinSplitSlices), kMaxSplit);
+  if (S < 2) return t;
+  t.full = total - r;
+  t.r = r;
+  t.S = S;
+  return t;
+}
 
 // ---------------------------------------------------------------------------------------------
 // Direct-to-LDS variant: the global -> LDS copies are global_load_lds_dwordx4 (each wave
@@ -94,15 +125,28 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
   const int mrow0 = wm * (BMT / WM);               // this wave's first row of the m-block
 
   const int nblk = (g.n_out + BNA - 1) / BNA;      // the last n-block may be ragged
-  const int logical = xcd_chunked<kChunk>(blockIdx.x, *g.num_tiles * nblk);
-  if (logical < 0) return;
+  const int KT_all = g.K / BK;
+  const TailSplit ts = tail_split(*g.num_tiles * nblk, g.slots, KT_all);
+  int logical, kbeg = 0, kend = KT_all, unit = -1;
+  if ((int)blockIdx.x < g.grid_tiles) {
+    logical = xcd_chunked<kChunk>(blockIdx.x, ts.full);
+    if (logical < 0) return;
+  } else {                                         // K-split unit of a last-round tile
+    const int u = (int)blockIdx.x - g.grid_tiles;
+    if (u >= ts.r * ts.S) return;
+    const int ti = u % ts.r, part = u / ts.r;
+    logical = ts.full + ti;
+    kbeg = part * KT_all / ts.S;
+    kend = (part + 1) * KT_all / ts.S;
+    unit = ti * ts.S + part;
+  }
   int mt, nt;
   grouped_tile<BMT, GROUP_M>(logical, nblk, g.tiles, g.offsets, mt, nt);
   const int e = g.tiles[2 * mt];
   const int row0 = g.tiles[2 * mt + 1];
   const int n0 = nt * BNA;
   const int K = g.K;
-  const int KT = K / BK;
+  const int KT = kend - kbeg;                       // k-slices of this workgroup, from kbeg
 
   // ---- this wave's copies: source row pointers (k-slice 0) and LDS offsets -----------------
   const char* src[NQW];
@@ -219,7 +263,7 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
     // stage of slice kt, which is refilled at once with slice kt+NS; the last k-step's MFMAs
     // then overlap the reads of slice kt+1's first fragments.  NS-1 slices stay in flight.
     #pragma unroll
-    for (int s = 0; s < NS; ++s) issue(s, min(s, KT - 1));
+    for (int s = 0; s < NS; ++s) issue(s, kbeg + min(s, KT - 1));
     wait_vmcnt<(NS - 1) * NQW>();
     __syncthreads();
     read_frags(a0, b0, 0, 0);
@@ -233,7 +277,7 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
       __syncthreads();
       // past the last slice repeat slice KT-1 (in bounds, never read) so every iteration
       // leaves the same number of copies outstanding
-      issue(buf, min(kt + NS, KT - 1));
+      issue(buf, kbeg + min(kt + NS, KT - 1));
       step(KK - 1, buf, nbuf);              // after the last slice the reads are stale, unused
       buf = nbuf;
     }
@@ -250,6 +294,22 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
   const int ocol = lane & 31;
   const int orow = 4 * (lane >> 5);
   const int ncol0 = n0 + wn * WTN;
+  if (!UP && unit >= 0) {
+    // K-split unit: the fp32 partial tile [BMT][BNA]; all-padding fragments are not stored
+    // (split_reduce_kernel reads only rows that hold slots)
+    float* pb = g.part + (size_t)unit * BMT * BNA + wn * WTN + ocol;
+    #pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if (i >= fmv) continue;
+      #pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = mrow0 + i * 32 + 8 * (v >> 2) + orow + (v & 3);
+        #pragma unroll
+        for (int j = 0; j < FN; ++j) pb[(size_t)m * BNA + j * 32] = acc[i][j][v];
+      }
+    }
+    return;
+  }
   auto epilogue = [&](auto ragged_tag) {
     constexpr bool RAGGED = decltype(ragged_tag)::value;
     if (UP) {
@@ -289,13 +349,58 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
   else                        epilogue(std::true_type{});
 }
 
+// Sum of the S partial tiles of each K-split tile (ascending part order), times the routing
+// weight, rounded once to bf16: one wave per row, BNA/64 columns per lane, 16 rows per block.
+template <int BMT, int BNA>
+__global__ __launch_bounds__(256) void split_reduce_kernel(Args g) {
+  constexpr int CPL = BNA / kWave;
+  constexpr int RPB = 16;
+  const int nblk = (g.n_out + BNA - 1) / BNA;
+  const TailSplit ts = tail_split(*g.num_tiles * nblk, g.slots, g.K / kSplitBK);
+  const int ti = (int)blockIdx.x / (BMT / RPB);
+  if (ti >= ts.r) return;
+  int mt, nt;
+  grouped_tile<BMT, GROUP_M>(ts.full + ti, nblk, g.tiles, g.offsets, mt, nt);
+  const int row0 = g.tiles[2 * mt + 1];
+  const int n0 = nt * BNA;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c0 = lane * CPL;
+  const size_t pstride = (size_t)BMT * BNA;
+  for (int m = ((int)blockIdx.x % (BMT / RPB)) * RPB + (int)threadIdx.x / kWave;
+       m < ((int)blockIdx.x % (BMT / RPB) + 1) * RPB; m += 256 / kWave) {
+    const int s = g.sorted_slots[row0 + m];
+    if (s >= g.n_slots) continue;
+    const float* pb = g.part + (size_t)ti * ts.S * pstride + (size_t)m * BNA + c0;
+    float sum[CPL];
+    #pragma unroll
+    for (int c = 0; c < CPL; ++c) sum[c] = pb[c];
+    for (int p = 1; p < ts.S; ++p)
+      #pragma unroll
+      for (int c = 0; c < CPL; ++c) sum[c] += pb[p * pstride + c];
+    const float wt = g.topk_w[s];
+    uint16_t* dst = g.out + (size_t)s * g.n_out + n0 + c0;
+    #pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      if (n0 + c0 + c < g.n_out) dst[c] = (uint16_t)f32_to_bf16_bits(sum[c] * wt);
+  }
+}
+
 template <int BK, int NS, int BNA, bool UP, int WM = 1, int BMT = BM, int WN = 4>
-hipError_t run_dma(const Args& a, hipStream_t s) {
+hipError_t run_dma(Args a, hipStream_t s) {
   // sized by the host-side tile bound; blocks past the device-side tile count exit at once
   const int64_t grid = xcd_chunked_grid<kChunk>((int64_t)a.tiles_max * ((a.n_out + BNA - 1) / BNA));
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_dma_kernel<BMT, BK, NS, BNA, UP, WM, WN>), dim3((unsigned)grid),
-                     dim3(WN * WM * kWave), 0, s, a);
+  const bool split = !UP && a.part != nullptr && a.slots >= 2;
+  if (!split) a.slots = 0;
+  static_assert(UP || BK == kSplitBK, "the K-split tail assumes 64-wide k-slices");
+  a.grid_tiles = (int)grid;
+  hipLaunchKernelGGL((gemm_dma_kernel<BMT, BK, NS, BNA, UP, WM, WN>),
+                     dim3((unsigned)(grid + (split ? a.slots : 0))), dim3(WN * WM * kWave), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !split) return e;
+  // S >= 2 needs r <= slots / 2 tiles to reduce
+  hipLaunchKernelGGL((split_reduce_kernel<BMT, BNA>), dim3((unsigned)(a.slots / 2 * (BMT / 16))),
+                     dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -304,6 +409,14 @@ hipError_t run_dma(const Args& a, hipStream_t s) {
 // bf16 with 128- or 256-row m-blocks.
 bool prefill_supported(const Resolved& r) {
   return r.w_dtype == MOE_BF16 && (r.BM == pf::BM || r.BM == 2 * pf::BM);
+}
+
+// Partial-tile buffer of the down GEMM's K-split tail: kMaxSplitUnits fp32 tiles of block_m
+// rows x the down launch's n-block width (256 when H allows, else 128).
+int64_t down_split_bytes(const Resolved& r) {
+  if (!prefill_supported(r)) return 0;
+  const int64_t bna = r.H % 256 == 0 ? 256 : 128;
+  return (int64_t)pf::kMaxSplitUnits * r.BM * bna * 4;
 }
 
 hipError_t launch_up_prefill(const Resolved& r, const void* x, const void* w13,
@@ -334,8 +447,11 @@ hipError_t launch_up_prefill(const Resolved& r, const void* x, const void* w13,
 hipError_t launch_down_prefill(const Resolved& r, const void* act, const void* w2,
                                const float* topk_w, const int32_t* sorted_slots,
                                const int32_t* offsets, const int32_t* tiles,
-                               const int32_t* num_tiles, void* slot_out, hipStream_t s) {
+                               const int32_t* num_tiles, void* slot_out, void* split_ws,
+                               hipStream_t s) {
   pf::Args a{};
+  a.part = (float*)split_ws;
+  a.slots = split_ws ? std::min(device_cu_count(), pf::kMaxSplitUnits) : 0;
   a.offsets = offsets;
   a.a_src = (const char*)act;
   a.w = (const char*)w2;

@@ -224,10 +224,15 @@ hipError_t launch_up(const Resolved& r, const void* x, const float* x_scales, co
                      const int32_t* tiles, const int32_t* num_tiles, void* act, float* act_scales,
                      hipStream_t s);
 
+// split_ws: partial-tile buffer of down_split_bytes(r) bytes for the K-split tail of the
+// 128/256-row bf16 down GEMM, or null (no split).
 hipError_t launch_down(const Resolved& r, const void* act, const float* act_scales,
                        const void* w2, const float* w2_scales, const float* topk_w,
                        const int32_t* sorted_slots, const int32_t* offsets, const int32_t* tiles,
-                       const int32_t* num_tiles, void* slot_out, hipStream_t s);
+                       const int32_t* num_tiles, void* slot_out, void* split_ws, hipStream_t s);
+int64_t down_split_bytes(const Resolved& r);
+// Compute units of the current device (cached per device ordinal).
+int device_cu_count();
 
 // bf16 kernels for 128-row m-blocks (MFMA 32x32x16), used by launch_up / launch_down.
 bool prefill_supported(const Resolved& r);
@@ -238,7 +243,8 @@ hipError_t launch_up_prefill(const Resolved& r, const void* x, const void* w13,
 hipError_t launch_down_prefill(const Resolved& r, const void* act, const void* w2,
                                const float* topk_w, const int32_t* sorted_slots,
                                const int32_t* offsets, const int32_t* tiles,
-                               const int32_t* num_tiles, void* slot_out, hipStream_t s);
+                               const int32_t* num_tiles, void* slot_out, void* split_ws,
+                               hipStream_t s);
 
 // Weight-streaming kernels (bf16 m-blocks of 16..64 rows, e4m3 m-blocks of 128 rows).
 bool stream_supported(const Resolved& r);
