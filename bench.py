@@ -230,7 +230,7 @@ def sweep(args):
             act = torch.empty((moe.moe_max_padded_slots(p), I), dtype=torch.bfloat16, device=dev)
             slot_out = torch.empty((T * K, H), dtype=torch.bfloat16, device=dev)
             out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-            dws = moe.alloc_down_workspace(p, dev)
+            dws = moe.alloc_gemm_workspace(p, dev)
 
             def step(ev=None):
                 if ev: ev[0].record()
@@ -238,7 +238,7 @@ def sweep(args):
                               a["tiles"], a["num_tiles"], a["n_invalid"])
                 if ev: ev[1].record()
                 moe.moe_grouped_gemm_up(p, x, None, case.w13, None, a["sorted_slots"], a["offsets"],
-                                        a["tiles"], a["num_tiles"], act, None)
+                                        a["tiles"], a["num_tiles"], act, None, dws)
                 if ev: ev[2].record()
                 moe.moe_grouped_gemm_down(p, act, None, case.w2, None, wts, a["sorted_slots"],
                                           a["offsets"], a["tiles"], a["num_tiles"], slot_out, dws)
@@ -456,7 +456,7 @@ def main():
     slot_out = torch.empty((cfg.T * cfg.top_k, cfg.H), dtype=case.x.dtype, device=dev)
     out = torch.empty((cfg.T, cfg.H), dtype=case.x.dtype, device=dev)
     ws = moe.alloc_workspace(p, dev)
-    down_ws = moe.alloc_down_workspace(p, dev)
+    gemm_ws = moe.alloc_gemm_workspace(p, dev)
     routing = args.routing == "on"
     if routing:
         from moe_inputs import make_logits
@@ -488,12 +488,12 @@ def main():
             x_in = xq
             mark()
         moe.moe_grouped_gemm_up(p, x_in, x_scales, case.w13, case.w13_scales, a["sorted_slots"], a["offsets"],
-                                a["tiles"], a["num_tiles"], act, act_scales)
+                                a["tiles"], a["num_tiles"], act, act_scales, gemm_ws)
         mark()
         moe.moe_grouped_gemm_down(p, act, act_scales, case.w2, case.w2_scales,
                                   r_w if routing else case.topk_weights,
                                   a["sorted_slots"], a["offsets"], a["tiles"], a["num_tiles"], slot_out,
-                                  down_ws)
+                                  gemm_ws)
         mark()
         moe.moe_combine(p, slot_out, a["slot_row"], out)
         mark()

@@ -203,11 +203,14 @@ int moe_quantize_rows_e4m3(const moe_problem* p, const void* x, uint8_t* xq, flo
  *               act_scales fp32 [moe_max_padded_slots, I/128] (amax/448 per row and
  *               128-column group, as above).  Rows of valid tiles are written (padding
  *               rows get 0); rows past the last valid tile are left untouched.
+ * workspace: NULL, or the optional GEMM workspace described at moe_gemm_workspace_bytes
+ *      (MOE_ERR_WORKSPACE if smaller, MOE_ERR_ALIGN if not 256-byte aligned).
  */
 int moe_grouped_gemm_up(const moe_problem* p, const void* x, const float* x_scales,
                         const void* w13, const float* w13_scales, const int32_t* sorted_slots,
                         const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles,
-                        void* act, float* act_scales, void* stream);
+                        void* act, float* act_scales, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /*
  * moe_grouped_gemm_up_mxfp4 -- the up projection of the "MOE Bmm1 Fused Gather"
@@ -251,13 +254,8 @@ int moe_grouped_gemm_up_mxfp4(const moe_problem* p, const uint8_t* x, const floa
  *      sorted_slots, offsets, tiles, num_tiles: outputs of moe_align for the same problem
  * Out: slot_out dtype [N, H] (bf16 for E4M3 weights).  Rows of excluded slots
  *      are not written.
- * workspace: NULL, or device memory of at least moe_down_workspace_bytes(p) bytes,
- *      256-byte aligned (MOE_ERR_WORKSPACE if smaller, MOE_ERR_ALIGN if misaligned);
- *      caller-owned scratch whose contents are unspecified afterwards.  With it, bf16
- *      problems of 128- or 256-row m-blocks cut the tiles of the GEMM's last, partly
- *      filled round of workgroups along K into parts whose fp32 partial sums are added
- *      in a fixed order: the result is deterministic, but its rounding differs from a
- *      call without workspace.  Calls that share a workspace must not overlap.
+ * workspace: NULL, or the optional GEMM workspace described at moe_gemm_workspace_bytes
+ *      (MOE_ERR_WORKSPACE if smaller, MOE_ERR_ALIGN if not 256-byte aligned).
  */
 int moe_grouped_gemm_down(const moe_problem* p, const void* act, const float* act_scales,
                           const void* w2, const float* w2_scales, const float* topk_weights,
@@ -265,9 +263,17 @@ int moe_grouped_gemm_down(const moe_problem* p, const void* act, const float* ac
                           const int32_t* tiles, const int32_t* num_tiles, void* slot_out,
                           void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of the optional workspace of moe_grouped_gemm_down (0: the problem's down GEMM
- * never uses one); negative moe_status for an invalid problem. */
-int64_t moe_down_workspace_bytes(const moe_problem* p);
+/*
+ * Bytes of the optional workspace of moe_grouped_gemm_up and moe_grouped_gemm_down (0: the
+ * problem's GEMMs never use one); negative moe_status for an invalid problem.
+ * The workspace is device memory, 256-byte aligned, caller-owned scratch whose contents are
+ * unspecified afterwards; calls that share one must not overlap.  With it, bf16 problems of
+ * 128- or 256-row m-blocks cut the tiles of a GEMM's last, partly filled round of workgroups
+ * (one per compute unit) along K into parts whose fp32 partial tiles are added in a fixed
+ * order before the epilogue: the result is deterministic, but its rounding differs from a
+ * call without workspace.  moe_forward carves the same buffer out of its own workspace.
+ */
+int64_t moe_gemm_workspace_bytes(const moe_problem* p);
 
 /*
  * moe_combine -- deterministic per-token combine, no atomics.

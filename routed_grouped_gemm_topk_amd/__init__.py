@@ -33,7 +33,7 @@ from ._lib import (  # noqa: F401
     moe_align,
     moe_block_m_for,
     moe_combine,
-    moe_down_workspace_bytes,
+    moe_gemm_workspace_bytes,
     moe_forward,
     moe_grouped_gemm_down,
     moe_grouped_gemm_up,
@@ -90,9 +90,10 @@ def alloc_workspace(p: Problem, device) -> torch.Tensor:
     return torch.empty(moe_workspace_bytes(p), dtype=torch.uint8, device=device)
 
 
-def alloc_down_workspace(p: Problem, device) -> Optional[torch.Tensor]:
-    """The optional workspace of moe_grouped_gemm_down (None when the problem needs none)."""
-    n = moe_down_workspace_bytes(p)
+def alloc_gemm_workspace(p: Problem, device) -> Optional[torch.Tensor]:
+    """The optional workspace of moe_grouped_gemm_up / _down (None when the problem's GEMMs
+    use none)."""
+    n = moe_gemm_workspace_bytes(p)
     return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
 
 

@@ -33,7 +33,7 @@ _TORCH_DT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_E4M3: torch.f
 EXPORTS = ["moe_status_str", "moe_validate", "moe_pick_block_m", "moe_block_m_for", "moe_max_padded_slots",
            "moe_max_tiles", "moe_workspace_bytes", "moe_route", "moe_route_align", "moe_align",
            "moe_quantize_rows_e4m3", "moe_grouped_gemm_up", "moe_grouped_gemm_up_mxfp4",
-           "moe_grouped_gemm_down", "moe_down_workspace_bytes",
+           "moe_grouped_gemm_down", "moe_gemm_workspace_bytes",
            "moe_combine", "moe_forward"]
 
 
@@ -88,11 +88,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "moe_route": (ctypes.c_int, [P, vp, ctypes.c_int, vp, vp, vp]),
         "moe_route_align": (ctypes.c_int, [P, vp, ctypes.c_int] + [vp] * 9 + [vp]),
         "moe_quantize_rows_e4m3": (ctypes.c_int, [P, vp, vp, vp, vp]),
-        "moe_grouped_gemm_up": (ctypes.c_int, [P] + [vp] * 10 + [vp]),
+        "moe_grouped_gemm_up": (ctypes.c_int, [P] + [vp] * 11 + [ctypes.c_size_t, vp]),
         "moe_grouped_gemm_up_mxfp4": (ctypes.c_int, [P] + [vp] * 5 + [ctypes.c_float] * 2
                                       + [vp] * 6 + [vp]),
         "moe_grouped_gemm_down": (ctypes.c_int, [P] + [vp] * 11 + [ctypes.c_size_t, vp]),
-        "moe_down_workspace_bytes": (ctypes.c_int64, [P]),
+        "moe_gemm_workspace_bytes": (ctypes.c_int64, [P]),
         "moe_combine": (ctypes.c_int, [P, vp, vp, vp, vp]),
         "moe_forward": (ctypes.c_int, [P] + [vp] * 9 + [ctypes.c_size_t, vp]),
     }
@@ -144,8 +144,8 @@ def moe_workspace_bytes(p: Problem) -> int:
     return _checked(load().moe_workspace_bytes(ctypes.byref(p)), "moe_workspace_bytes")
 
 
-def moe_down_workspace_bytes(p: Problem) -> int:
-    return _checked(load().moe_down_workspace_bytes(ctypes.byref(p)), "moe_down_workspace_bytes")
+def moe_gemm_workspace_bytes(p: Problem) -> int:
+    return _checked(load().moe_gemm_workspace_bytes(ctypes.byref(p)), "moe_gemm_workspace_bytes")
 
 
 # ---------------------------------------------------------------------------------------------
@@ -232,7 +232,7 @@ def moe_quantize_rows_e4m3(p: Problem, x, xq, scales, stream=None) -> None:
 
 
 def moe_grouped_gemm_up(p: Problem, x, x_scales, w13, w13_scales, sorted_slots, offsets, tiles,
-                        num_tiles, act, act_scales, stream=None) -> None:
+                        num_tiles, act, act_scales, workspace=None, stream=None) -> None:
     rows = moe_max_padded_slots(p)
     fp8 = p.w_dtype == MOE_E4M3
     xdt = (torch.uint8, torch.float8_e4m3fn) if fp8 else _TORCH_DT[p.dtype]
@@ -245,7 +245,9 @@ def moe_grouped_gemm_up(p: Problem, x, x_scales, w13, w13_scales, sorted_slots, 
             _ptr(tiles, "tiles", torch.int32, 2 * moe_max_tiles(p)),
             _ptr(num_tiles, "num_tiles", torch.int32, 1),
             _ptr(act, "act", (_act_dtype(p), torch.float8_e4m3fn) if fp8 else _act_dtype(p), rows * p.I),
-            _ptr(act_scales, "act_scales", torch.float32, rows * p.I // 128)]
+            _ptr(act_scales, "act_scales", torch.float32, rows * p.I // 128),
+            _ptr(workspace, "workspace", torch.uint8),
+            0 if workspace is None else workspace.numel() * workspace.element_size()]
     _checked(load().moe_grouped_gemm_up(ctypes.byref(p), *args, _stream(stream)),
              "moe_grouped_gemm_up")
 

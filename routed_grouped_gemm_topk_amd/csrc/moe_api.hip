@@ -111,7 +111,7 @@ Layout layout(const Resolved& r) {
   L.act = take(r.rows_max * r.I * (fp8 ? 1 : elt_bytes(r.dtype)));
   L.act_scales = fp8 ? take(4LL * r.rows_max * (r.I / kGroup)) : -1;
   L.slot_out = take(r.N * r.H * elt_bytes(r.dtype));
-  const int64_t split = down_split_bytes(r);
+  const int64_t split = gemm_split_bytes(r);
   L.split = split > 0 ? take(split) : -1;
   L.total = o;
   return L;
@@ -201,11 +201,11 @@ int64_t moe_max_tiles(const moe_problem* p) {
   return v != MOE_OK ? v : resolve(p).tiles_max;
 }
 
-int64_t moe_down_workspace_bytes(const moe_problem* p) {
+int64_t moe_gemm_workspace_bytes(const moe_problem* p) {
   const int v = validate(p);
   if (v != MOE_OK) return v;
   if (is_mx(p)) return MOE_ERR_DTYPE;
-  return down_split_bytes(resolve(p));
+  return gemm_split_bytes(resolve(p));
 }
 
 int64_t moe_workspace_bytes(const moe_problem* p) {
@@ -279,18 +279,24 @@ int moe_quantize_rows_e4m3(const moe_problem* p, const void* x, uint8_t* xq, flo
 int moe_grouped_gemm_up(const moe_problem* p, const void* x, const float* x_scales,
                         const void* w13, const float* w13_scales, const int32_t* sorted_slots,
                         const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles,
-                        void* act, float* act_scales, void* stream) {
+                        void* act, float* act_scales, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   int v = validate(p);
   if (v) return v;
   if (is_mx(p)) return MOE_ERR_DTYPE;
   if (!x || !w13 || !sorted_slots || !offsets || !tiles || !num_tiles || !act) return MOE_ERR_NULL;
   if (p->w_dtype == MOE_E4M3 && (!x_scales || !w13_scales || !act_scales)) return MOE_ERR_NULL;
+  const Resolved r = resolve(p);
+  const int64_t split = gemm_split_bytes(r);
+  if (workspace && (int64_t)workspace_bytes < split) return MOE_ERR_WORKSPACE;
   if ((v = check_align({{x, 16}, {x_scales, 4}, {w13, 16}, {w13_scales, 4}, {sorted_slots, 4},
-                        {offsets, 4}, {tiles, 4}, {num_tiles, 4}, {act, 16}, {act_scales, 4}})))
+                        {offsets, 4}, {tiles, 4}, {num_tiles, 4}, {act, 16}, {act_scales, 4},
+                        {workspace, 256}})))
     return v;
   if ((v = check_device())) return v;
-  return status_of(launch_up(resolve(p), x, x_scales, w13, w13_scales, sorted_slots, offsets,
-                             tiles, num_tiles, act, act_scales, (hipStream_t)stream));
+  return status_of(launch_up(r, x, x_scales, w13, w13_scales, sorted_slots, offsets, tiles,
+                             num_tiles, act, act_scales, split > 0 ? workspace : nullptr,
+                             (hipStream_t)stream));
 }
 
 int moe_grouped_gemm_up_mxfp4(const moe_problem* p, const uint8_t* x, const float* x_scale,
@@ -328,7 +334,7 @@ int moe_grouped_gemm_down(const moe_problem* p, const void* act, const float* ac
     return MOE_ERR_NULL;
   if (p->w_dtype == MOE_E4M3 && (!act_scales || !w2_scales)) return MOE_ERR_NULL;
   const Resolved r = resolve(p);
-  const int64_t split = down_split_bytes(r);
+  const int64_t split = gemm_split_bytes(r);
   if (workspace && (int64_t)workspace_bytes < split) return MOE_ERR_WORKSPACE;
   if ((v = check_align({{act, 16}, {act_scales, 4}, {w2, 16}, {w2_scales, 4}, {topk_weights, 4},
                         {sorted_slots, 4}, {offsets, 4}, {tiles, 4}, {num_tiles, 4},
@@ -392,7 +398,7 @@ int moe_forward(const moe_problem* p, const void* x, const int32_t* topk_ids,
     x_scales = (const float*)at(L.x_scales);
   }
   e = launch_up(r, x_in, x_scales, w13, w13_scales, sorted_slots, offsets, tiles, num_tiles,
-                at(L.act), (float*)at(L.act_scales), s);
+                at(L.act), (float*)at(L.act_scales), at(L.split), s);
   if (e != hipSuccess) return MOE_ERR_LAUNCH;
   e = launch_down(r, at(L.act), (const float*)at(L.act_scales), w2, w2_scales, topk_weights,
                   sorted_slots, offsets, tiles, num_tiles, at(L.slot_out), at(L.split), s);

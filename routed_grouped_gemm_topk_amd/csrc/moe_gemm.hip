@@ -380,9 +380,9 @@ static hipError_t dispatch_bm(const Resolved& r, const GemmArgs& a, hipStream_t 
 hipError_t launch_up(const Resolved& r, const void* x, const float* x_scales, const void* w13,
                      const float* w13_scales, const int32_t* sorted_slots, const int32_t* offsets,
                      const int32_t* tiles, const int32_t* num_tiles, void* act, float* act_scales,
-                     hipStream_t s) {
+                     void* split_ws, hipStream_t s) {
   if (prefill_supported(r))
-    return launch_up_prefill(r, x, w13, sorted_slots, offsets, tiles, num_tiles, act, s);
+    return launch_up_prefill(r, x, w13, sorted_slots, offsets, tiles, num_tiles, act, split_ws, s);
   if (stream_supported(r))
     return launch_up_stream(r, x, x_scales, w13, w13_scales, sorted_slots, offsets, tiles,
                             num_tiles, act, act_scales, s);

@@ -56,20 +56,20 @@ struct Args {
   const int32_t* num_tiles;
   const float* topk_w;      // down
   uint16_t* out;            // up: act [rows_max, I]; down: slot_out [N, H]  (bf16 bits)
-  float* part;              // down: fp32 partial tiles of the K-split tail, or null
+  float* part;              // fp32 partial tiles of the K-split tail, or null
   int K, n_out, top_k, n_slots, tiles_max;
-  int slots;                // down with part: workgroup slots of the device (one per CU), else 0
+  int slots;                // with part: workgroup slots of the device (one per CU), else 0
   int grid_tiles;           // blocks [0, grid_tiles) run whole tiles, the rest K-split units
   int64_t w_expert_elems;
 };
 
-// K-split of the last round (down GEMM).  The logical tiles run in rounds of `slots`
+// K-split of the last round.  The logical tiles run in rounds of `slots`
 // workgroups (one per CU); when the last round holds only r < slots tiles, those r tiles
 // are cut along K into S parts, S = min(slots / r, K slices / kMinSplitSlices, kMaxSplit),
 // so the last round is r*S short units instead of r whole tiles beside idle CUs.  Each unit
 // writes its fp32 partial tile; split_reduce_kernel adds the S partials of a row in
-// ascending part order (fixed, so the result does not depend on timing), applies the
-// routing weight and rounds once.
+// ascending part order (fixed, so the result does not depend on timing), then applies the
+// epilogue (up: SiLU(gate) * up; down: the routing weight) and rounds once.
 constexpr int kSplitBK = 64;          // k-slice of every prefill launch that may split
 constexpr int kMinSplitSlices = 8;    // at least 512 of K per part
 constexpr int kMaxSplit = 16;
@@ -294,10 +294,12 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
   const int ocol = lane & 31;
   const int orow = 4 * (lane >> 5);
   const int ncol0 = n0 + wn * WTN;
-  if (!UP && unit >= 0) {
-    // K-split unit: the fp32 partial tile [BMT][BNA]; all-padding fragments are not stored
-    // (split_reduce_kernel reads only rows that hold slots)
-    float* pb = g.part + (size_t)unit * BMT * BNA + wn * WTN + ocol;
+  if (unit >= 0) {
+    // K-split unit: the fp32 partial tile [BMT][PW] (up: gate columns, then up columns);
+    // all-padding fragments are not stored (split_reduce_kernel reads only rows that hold
+    // slots)
+    constexpr int PW = UP ? 2 * BNA : BNA;
+    float* pb = g.part + (size_t)unit * BMT * PW + wn * WTN + ocol;
     #pragma unroll
     for (int i = 0; i < FM; ++i) {
       if (i >= fmv) continue;
@@ -305,7 +307,8 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
       for (int v = 0; v < 16; ++v) {
         const int m = mrow0 + i * 32 + 8 * (v >> 2) + orow + (v & 3);
         #pragma unroll
-        for (int j = 0; j < FN; ++j) pb[(size_t)m * BNA + j * 32] = acc[i][j][v];
+        for (int j = 0; j < NF; ++j)
+          pb[(size_t)m * PW + (j < FN ? j * 32 : BNA + (j - FN) * 32)] = acc[i][j][v];
       }
     }
     return;
@@ -349,12 +352,14 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
   else                        epilogue(std::true_type{});
 }
 
-// Sum of the S partial tiles of each K-split tile (ascending part order), times the routing
-// weight, rounded once to bf16: one wave per row, BNA/64 columns per lane, 16 rows per block.
-template <int BMT, int BNA>
+// Sum of the S partial tiles of each K-split tile (ascending part order), then the epilogue
+// (up: SiLU(gate) * up, padding rows 0; down: times the routing weight, padding rows not
+// stored), rounded once to bf16: one wave per row, BNA/64 columns per lane, 16 rows per block.
+template <int BMT, int BNA, bool UP>
 __global__ __launch_bounds__(256) void split_reduce_kernel(Args g) {
   constexpr int CPL = BNA / kWave;
   constexpr int RPB = 16;
+  constexpr int PW = UP ? 2 * BNA : BNA;
   const int nblk = (g.n_out + BNA - 1) / BNA;
   const TailSplit ts = tail_split(*g.num_tiles * nblk, g.slots, g.K / kSplitBK);
   const int ti = (int)blockIdx.x / (BMT / RPB);
@@ -365,23 +370,45 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(Args g) {
   const int n0 = nt * BNA;
   const int lane = threadIdx.x & (kWave - 1);
   const int c0 = lane * CPL;
-  const size_t pstride = (size_t)BMT * BNA;
+  const size_t pstride = (size_t)BMT * PW;
   for (int m = ((int)blockIdx.x % (BMT / RPB)) * RPB + (int)threadIdx.x / kWave;
        m < ((int)blockIdx.x % (BMT / RPB) + 1) * RPB; m += 256 / kWave) {
     const int s = g.sorted_slots[row0 + m];
-    if (s >= g.n_slots) continue;
-    const float* pb = g.part + (size_t)ti * ts.S * pstride + (size_t)m * BNA + c0;
-    float sum[CPL];
-    #pragma unroll
-    for (int c = 0; c < CPL; ++c) sum[c] = pb[c];
-    for (int p = 1; p < ts.S; ++p)
+    if (UP) {
+      uint16_t* dst = g.out + (size_t)(row0 + m) * g.n_out + n0 + c0;
+      float gt[CPL], up[CPL];
       #pragma unroll
-      for (int c = 0; c < CPL; ++c) sum[c] += pb[p * pstride + c];
-    const float wt = g.topk_w[s];
-    uint16_t* dst = g.out + (size_t)s * g.n_out + n0 + c0;
-    #pragma unroll
-    for (int c = 0; c < CPL; ++c)
-      if (n0 + c0 + c < g.n_out) dst[c] = (uint16_t)f32_to_bf16_bits(sum[c] * wt);
+      for (int c = 0; c < CPL; ++c) gt[c] = up[c] = 0.0f;
+      if (s < g.n_slots) {
+        const float* pb = g.part + (size_t)ti * ts.S * pstride + (size_t)m * PW + c0;
+        for (int p = 0; p < ts.S; ++p)
+          #pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            gt[c] += pb[p * pstride + c];
+            up[c] += pb[p * pstride + BNA + c];
+          }
+      }
+      #pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        if (n0 + c0 + c < g.n_out) {
+          const float a = gt[c] * __builtin_amdgcn_rcpf(1.0f + __expf(-gt[c])) * up[c];
+          dst[c] = (uint16_t)f32_to_bf16_bits(a);
+        }
+    } else {
+      if (s >= g.n_slots) continue;
+      const float* pb = g.part + (size_t)ti * ts.S * pstride + (size_t)m * PW + c0;
+      float sum[CPL];
+      #pragma unroll
+      for (int c = 0; c < CPL; ++c) sum[c] = pb[c];
+      for (int p = 1; p < ts.S; ++p)
+        #pragma unroll
+        for (int c = 0; c < CPL; ++c) sum[c] += pb[p * pstride + c];
+      const float wt = g.topk_w[s];
+      uint16_t* dst = g.out + (size_t)s * g.n_out + n0 + c0;
+      #pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        if (n0 + c0 + c < g.n_out) dst[c] = (uint16_t)f32_to_bf16_bits(sum[c] * wt);
+    }
   }
 }
 
@@ -390,16 +417,16 @@ hipError_t run_dma(Args a, hipStream_t s) {
   // sized by the host-side tile bound; blocks past the device-side tile count exit at once
   const int64_t grid = xcd_chunked_grid<kChunk>((int64_t)a.tiles_max * ((a.n_out + BNA - 1) / BNA));
   if (grid <= 0) return hipSuccess;
-  const bool split = !UP && a.part != nullptr && a.slots >= 2;
+  const bool split = a.part != nullptr && a.slots >= 2;
   if (!split) a.slots = 0;
-  static_assert(UP || BK == kSplitBK, "the K-split tail assumes 64-wide k-slices");
+  static_assert(BK == kSplitBK, "the K-split tail assumes 64-wide k-slices");
   a.grid_tiles = (int)grid;
   hipLaunchKernelGGL((gemm_dma_kernel<BMT, BK, NS, BNA, UP, WM, WN>),
                      dim3((unsigned)(grid + (split ? a.slots : 0))), dim3(WN * WM * kWave), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
   // S >= 2 needs r <= slots / 2 tiles to reduce
-  hipLaunchKernelGGL((split_reduce_kernel<BMT, BNA>), dim3((unsigned)(a.slots / 2 * (BMT / 16))),
+  hipLaunchKernelGGL((split_reduce_kernel<BMT, BNA, UP>), dim3((unsigned)(a.slots / 2 * (BMT / 16))),
                      dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -411,19 +438,23 @@ bool prefill_supported(const Resolved& r) {
   return r.w_dtype == MOE_BF16 && (r.BM == pf::BM || r.BM == 2 * pf::BM);
 }
 
-// Partial-tile buffer of the down GEMM's K-split tail: kMaxSplitUnits fp32 tiles of block_m
-// rows x the down launch's n-block width (256 when H allows, else 128).
-int64_t down_split_bytes(const Resolved& r) {
+// Partial-tile buffer of the GEMMs' K-split tail: kMaxSplitUnits fp32 tiles of block_m rows
+// x the widest partial tile of the two launches (up: gate + up columns, 2 x 128 at 256-row
+// m-blocks, 2 x 256 or 2 x 128 at 128-row ones; down: 256 when H allows, else 128).
+int64_t gemm_split_bytes(const Resolved& r) {
   if (!prefill_supported(r)) return 0;
-  const int64_t bna = r.H % 256 == 0 ? 256 : 128;
-  return (int64_t)pf::kMaxSplitUnits * r.BM * bna * 4;
+  const int64_t up = r.BM == 256 ? 256 : (r.I % 256 == 0 ? 512 : 256);
+  const int64_t down = r.H % 256 == 0 ? 256 : 128;
+  return (int64_t)pf::kMaxSplitUnits * r.BM * (up > down ? up : down) * 4;
 }
 
 hipError_t launch_up_prefill(const Resolved& r, const void* x, const void* w13,
                              const int32_t* sorted_slots, const int32_t* offsets,
                              const int32_t* tiles, const int32_t* num_tiles, void* act,
-                             hipStream_t s) {
+                             void* split_ws, hipStream_t s) {
   pf::Args a{};
+  a.part = (float*)split_ws;
+  a.slots = split_ws ? std::min(device_cu_count(), pf::kMaxSplitUnits) : 0;
   a.offsets = offsets;
   a.a_src = (const char*)x;
   a.w = (const char*)w13;

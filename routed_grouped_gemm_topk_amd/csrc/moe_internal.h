@@ -222,15 +222,15 @@ hipError_t launch_quant_rows(const Resolved& r, const void* x, uint8_t* xq, floa
 hipError_t launch_up(const Resolved& r, const void* x, const float* x_scales, const void* w13,
                      const float* w13_scales, const int32_t* sorted_slots, const int32_t* offsets,
                      const int32_t* tiles, const int32_t* num_tiles, void* act, float* act_scales,
-                     hipStream_t s);
+                     void* split_ws, hipStream_t s);
 
-// split_ws: partial-tile buffer of down_split_bytes(r) bytes for the K-split tail of the
-// 128/256-row bf16 down GEMM, or null (no split).
+// split_ws: partial-tile buffer of gemm_split_bytes(r) bytes for the K-split tail of the
+// 128/256-row bf16 GEMMs, or null (no split).
 hipError_t launch_down(const Resolved& r, const void* act, const float* act_scales,
                        const void* w2, const float* w2_scales, const float* topk_w,
                        const int32_t* sorted_slots, const int32_t* offsets, const int32_t* tiles,
                        const int32_t* num_tiles, void* slot_out, void* split_ws, hipStream_t s);
-int64_t down_split_bytes(const Resolved& r);
+int64_t gemm_split_bytes(const Resolved& r);
 // Compute units of the current device (cached per device ordinal).
 int device_cu_count();
 
@@ -239,7 +239,7 @@ bool prefill_supported(const Resolved& r);
 hipError_t launch_up_prefill(const Resolved& r, const void* x, const void* w13,
                              const int32_t* sorted_slots, const int32_t* offsets,
                              const int32_t* tiles, const int32_t* num_tiles, void* act,
-                             hipStream_t s);
+                             void* split_ws, hipStream_t s);
 hipError_t launch_down_prefill(const Resolved& r, const void* act, const void* w2,
                                const float* topk_w, const int32_t* sorted_slots,
                                const int32_t* offsets, const int32_t* tiles,

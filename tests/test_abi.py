@@ -80,14 +80,14 @@ def test_entry_points_reject_before_any_hip_call(lib):
     p = bad(H=100)
     P = ctypes.byref(p)
     assert lib.moe_align(P, *([None] * 9)) == moe.MOE_ERR_SHAPE
-    assert lib.moe_grouped_gemm_up(P, *([None] * 11)) == moe.MOE_ERR_SHAPE
+    assert lib.moe_grouped_gemm_up(P, *([None] * 11), 0, None) == moe.MOE_ERR_SHAPE
     assert lib.moe_grouped_gemm_down(P, *([None] * 11), 0, None) == moe.MOE_ERR_SHAPE
     assert lib.moe_combine(P, None, None, None, None) == moe.MOE_ERR_SHAPE
     assert lib.moe_forward(P, *([None] * 9), 0, None) == moe.MOE_ERR_SHAPE
     p = bad()
     P = ctypes.byref(p)
     assert lib.moe_align(P, *([None] * 9)) == moe.MOE_ERR_NULL
-    assert lib.moe_grouped_gemm_up(P, *([None] * 11)) == moe.MOE_ERR_NULL
+    assert lib.moe_grouped_gemm_up(P, *([None] * 11), 0, None) == moe.MOE_ERR_NULL
     assert lib.moe_grouped_gemm_down(P, *([None] * 11), 0, None) == moe.MOE_ERR_NULL
     assert lib.moe_combine(P, None, None, None, None) == moe.MOE_ERR_NULL
     assert lib.moe_quantize_rows_e4m3(P, 8, 8, 8, None) == moe.MOE_ERR_DTYPE   # bf16 weights
@@ -175,7 +175,7 @@ def test_mxfp4_problem_validation(lib):
     P = ctypes.byref(mxp)
     f = [ctypes.c_void_p(256)] * 16
     assert lib.moe_workspace_bytes(P) == moe.MOE_ERR_DTYPE
-    assert lib.moe_grouped_gemm_up(P, *f[:10], None) == moe.MOE_ERR_DTYPE
+    assert lib.moe_grouped_gemm_up(P, *f[:10], None, 0, None) == moe.MOE_ERR_DTYPE
     assert lib.moe_grouped_gemm_down(P, *f[:10], None, 0, None) == moe.MOE_ERR_DTYPE
     assert lib.moe_combine(P, *f[:3], None) == moe.MOE_ERR_DTYPE
     assert lib.moe_quantize_rows_e4m3(P, *f[:3], None) == moe.MOE_ERR_DTYPE
@@ -198,8 +198,8 @@ def test_misaligned_pointers_are_rejected_before_any_launch(lib):
     assert lib.moe_align(P, ok, ok, ok, ok, ok, ok, ok, odd2, None) == A
     assert lib.moe_route(P, odd2, 0, ok, ok, None) == A
     assert lib.moe_route_align(P, ok, 0, ok, ok, ok, ok, ok, ok, odd2, ok, ok, None) == A
-    assert lib.moe_grouped_gemm_up(P, odd8, None, ok, None, ok, ok, ok, ok, ok, None, None) == A
-    assert lib.moe_grouped_gemm_up(P, ok, None, ok, None, ok, ok, ok, ok, odd8, None, None) == A
+    assert lib.moe_grouped_gemm_up(P, odd8, None, ok, None, ok, ok, ok, ok, ok, None, None, 0, None) == A
+    assert lib.moe_grouped_gemm_up(P, ok, None, ok, None, ok, ok, ok, ok, odd8, None, None, 0, None) == A
     assert lib.moe_grouped_gemm_down(P, ok, None, odd8, None, ok, ok, ok, ok, ok, ok, None, 0, None) == A
     assert lib.moe_grouped_gemm_down(P, ok, None, ok, None, odd2, ok, ok, ok, ok, ok, None, 0, None) == A
     assert lib.moe_combine(P, ok, ok, odd8, None) == A
@@ -216,28 +216,37 @@ def test_misaligned_pointers_are_rejected_before_any_launch(lib):
     assert lib.moe_grouped_gemm_up_mxfp4(mxp, *args, None) == A           # act
 
 
-def test_down_workspace_size_and_checks(lib):
-    """moe_grouped_gemm_down's optional workspace: 256 fp32 partial tiles of block_m rows x the
-    down n-block (256 columns when H allows, else 128) for bf16 problems on the 128/256-row
-    kernels, 0 elsewhere; too small -> MOE_ERR_WORKSPACE, misaligned -> MOE_ERR_ALIGN, both on
-    the host."""
+def test_gemm_workspace_size_and_checks(lib):
+    """The GEMMs' optional workspace: 256 fp32 partial tiles of block_m rows x the widest
+    partial tile of the two launches (up: gate + up columns; down: the n-block) for bf16
+    problems on the 128/256-row kernels, 0 elsewhere; too small -> MOE_ERR_WORKSPACE,
+    misaligned -> MOE_ERR_ALIGN, both on the host."""
     big = moe.make_problem(4096, 4096, 14336, 8, 2, "bf16")               # block_m 256
     assert moe.moe_pick_block_m(big) == 256
-    assert moe.moe_down_workspace_bytes(big) == 256 * 256 * 256 * 4
-    assert moe.moe_down_workspace_bytes(moe.make_problem(4096, 2880, 2880, 8, 2, "bf16")) \
-        == 256 * 256 * 128 * 4                                               # H % 256 != 0
-    assert moe.moe_down_workspace_bytes(moe.make_problem(64, 7168, 2048, 256, 8, "bf16")) == 0
-    assert moe.moe_down_workspace_bytes(moe.make_problem(2048, 7168, 2048, 256, 8, "bf16", "e4m3")) == 0
-    assert moe.moe_down_workspace_bytes(moe.make_problem(16, 128, 256, 8, 2, "f32")) == 0
+    assert moe.moe_gemm_workspace_bytes(big) == 256 * 256 * 256 * 4
+    # H % 256 != 0: down n-block 128, up 2 x 128
+    assert moe.moe_gemm_workspace_bytes(moe.make_problem(4096, 2880, 2880, 8, 2, "bf16")) \
+        == 256 * 256 * 256 * 4
+    assert moe.moe_gemm_workspace_bytes(moe.make_problem(64, 7168, 2048, 256, 8, "bf16")) == 0
+    assert moe.moe_gemm_workspace_bytes(moe.make_problem(2048, 7168, 2048, 256, 8, "bf16", "e4m3")) == 0
+    assert moe.moe_gemm_workspace_bytes(moe.make_problem(16, 128, 256, 8, 2, "f32")) == 0
     # moe_forward carves the same buffer out of its own workspace
-    small = moe.make_problem(4096, 4096, 14336, 8, 2, "bf16", block_m=128)
     assert moe.moe_workspace_bytes(big) - moe.moe_workspace_bytes(moe.make_problem(
-        4096, 4096, 14336, 8, 2, "bf16", block_m=64)) >= moe.moe_down_workspace_bytes(big)
-    need = moe.moe_down_workspace_bytes(small)
-    assert need == 256 * 128 * 256 * 4
+        4096, 4096, 14336, 8, 2, "bf16", block_m=64)) >= moe.moe_gemm_workspace_bytes(big)
+    small = moe.make_problem(4096, 4096, 14336, 8, 2, "bf16", block_m=128)
+    need = moe.moe_gemm_workspace_bytes(small)
+    assert need == 256 * 128 * 512 * 4                                       # up: 2 x 256 columns
+    assert moe.moe_gemm_workspace_bytes(moe.make_problem(4096, 4096, 2880, 8, 2, "bf16",
+                                                         block_m=128)) == 256 * 128 * 256 * 4
     P = ctypes.byref(small)
     ok = ctypes.c_void_p(4096)
+    W, A = moe.MOE_ERR_WORKSPACE, moe.MOE_ERR_ALIGN
+    odd = ctypes.c_void_p(4096 + 64)
     assert lib.moe_grouped_gemm_down(P, ok, None, ok, None, ok, ok, ok, ok, ok, ok, ok, need - 1,
-                                     None) == moe.MOE_ERR_WORKSPACE
-    assert lib.moe_grouped_gemm_down(P, ok, None, ok, None, ok, ok, ok, ok, ok, ok,
-                                     ctypes.c_void_p(4096 + 64), need, None) == moe.MOE_ERR_ALIGN
+                                     None) == W
+    assert lib.moe_grouped_gemm_down(P, ok, None, ok, None, ok, ok, ok, ok, ok, ok, odd, need,
+                                     None) == A
+    assert lib.moe_grouped_gemm_up(P, ok, None, ok, None, ok, ok, ok, ok, ok, None, ok, need - 1,
+                                   None) == W
+    assert lib.moe_grouped_gemm_up(P, ok, None, ok, None, ok, ok, ok, ok, ok, None, odd, need,
+                                   None) == A
