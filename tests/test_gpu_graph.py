@@ -1,6 +1,7 @@
 """moe_forward captured in a HIP graph: every replay equals the eager result bit for bit, with
 eager work and synchronisations between the replays (the library records no memset, no
-allocation and no host synchronisation, so the whole layer is capturable)."""
+allocation and no host synchronisation, so the whole layer is capturable; the workspace is
+cleared before each replay, so the K-split partial tiles must be rewritten by every replay)."""
 import pytest
 import torch
 
@@ -11,6 +12,9 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("name,kw", [("mixtral_prefill_bf16", dict(T=300, H=256, I=384)),
+                                     # 256-row m-blocks whose GEMMs split their last round
+                                     # along K (partials in the workspace, a second launch)
+                                     ("mixtral_prefill_bf16", dict(T=512, H=1024, I=2048, E=4)),
                                      ("dsv3_fp8_e4m3", dict(T=200, H=512, I=256, E=16)),
                                      ("tiny_fp32", dict())])
 def test_forward_graph_replays_match_eager(device, name, kw):
