@@ -27,6 +27,8 @@ CASES = {
     "tail_bm256": (dict(T=4096, H=2048, I=1024, E=8, top_k=2), 256),
     # 128-wide ragged n-blocks (H = 2880) at 128-row m-blocks
     "ragged_bm128": (dict(T=640, H=2880, I=1024, E=4, top_k=2), 128),
+    # and at 256-row m-blocks (down n-block 128, up 2 x 128)
+    "ragged_bm256": (dict(T=384, H=2880, I=1024, E=4, top_k=2), 256),
 }
 
 
