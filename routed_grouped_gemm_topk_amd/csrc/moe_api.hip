@@ -151,7 +151,7 @@ int check_align(std::initializer_list<Al> ptrs) {
 }  // namespace
 
 // Every entry point runs check_device() before it launches, so the count is known here;
-// 0 (unknown) turns the down GEMM's K-split tail off.
+// 0 (unknown) turns the GEMMs' K-split tail off.
 int moe::device_cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;

@@ -18,7 +18,10 @@
 //     the 16-byte chunk c of row r sits at position c ^ ((r & 7) ^ ((r >> 3) & 1)),
 //     conflict-free for the fragment reads (32 consecutive rows at one k offset);
 //   * global -> LDS copies by direct-to-LDS DMA (below), NS-1 slices in flight;
-//   * fragment reads of the next 16-wide k step overlap the MFMAs of the current one;
+//   * fragment reads of the next 16-wide k step overlap the MFMAs of the current one, one
+//     read after each MFMA;
+//   * with a workspace, the tiles of the last, partly filled round of workgroups are cut
+//     along K (tail_split below), their fp32 partials added by split_reduce_kernel;
 //   * tile order: expert by expert, groups of 8 m-blocks of one expert sweep the n-blocks;
 //     that order is dealt to the XCDs (own L2 each) in chunks of 32 tiles, so concurrent
 //     workgroups of an XCD share rows and weights, and a hot expert's tiles spread over all
