@@ -181,11 +181,25 @@ def warm_up(step, n, min_seconds=0.1):
             torch.cuda.synchronize()
 
 
+SWEEP_KEY_NOTE = ("  bm: the shard's block size, keyed on its local slots per active local "
+                  "expert; page-key bm: the same rule keyed on T*k/E_total.")
+
+
+def shard_block_m(moe, n_loc, active, x_dtype, w_dtype):
+    """Block size of one expert-parallel shard, keyed on its own dispatch counts: the slots it
+    received per local expert that received any (an expert-parallel dispatch exchanges the
+    per-expert counts before the expert GEMMs, so the shard knows them on the host).  The
+    pages key the same rule on the global mean T*k/E_total, which does not see that a shard
+    holding the popular experts receives several times its share."""
+    return moe.moe_block_m_for(n_loc / max(active, 1), x_dtype, w_dtype)
+
+
 def sweep(args):
     """The 48-point batch sweep of one expert-parallel shard ("MOE Bmm1 Fused Gather", its bench:
     batch sizes and production-like routing).  Per batch size: the whole layer (align, up, down,
-    combine) at the block_m an expert-parallel caller gets from moe_block_m_for(T*k/E_total)
-    (or --block-m), and optionally at each block_m of --sweep-block-m; one JSON line per point
+    combine) at the shard's block_m (shard_block_m, or --block-m), and optionally at each
+    block_m of --sweep-block-m; one JSON line per point (with the block_m of the pages' key
+    T*k/E_total beside it)
     with the up kernel's and the layer's times, useful TFLOP/s (local slots only) and the up
     kernel's roofline fraction max(flops/peak, bytes/HBM peak) / time."""
     import numpy as np
@@ -258,8 +272,8 @@ def sweep(args):
             return bm_used, {"align": st(0, 1), "up": st(1, 2), "down": st(2, 3),
                              "combine": st(3, 4), "layer": st(0, 4)}
 
-        bm_ep = args.block_m or moe.moe_block_m_for(T * K / (base.route_experts or E), "bf16",
-                                                    base.w_dtype)
+        bm_page = moe.moe_block_m_for(T * K / (base.route_experts or E), "bf16", base.w_dtype)
+        bm_ep = args.block_m or shard_block_m(moe, n_loc, active, "bf16", base.w_dtype)
         bm0, t0 = run(bm_ep)
         best = None
         by_bm = {}
@@ -272,7 +286,8 @@ def sweep(args):
                 best = (bm, t)
         pt = {"sweep": base.name, "T": T, "tokens_per_expert": T * K // (base.route_experts or E),
               "local_slots": n_loc, "active_experts": active, "max_per_expert": int(counts.max()),
-              "block_m": bm0, **{f"{k}_ms": round(v, 5) for k, v in t0.items()},
+              "block_m": bm0, "page_key_block_m": bm_page,
+              **{f"{k}_ms": round(v, 5) for k, v in t0.items()},
               "up_TFLOP/s": round(up_flops / t0["up"] / 1e9, 1),
               "up_pct_mfma_peak": round(100 * up_flops / t0["up"] / 1e9 / peak_tf, 2),
               "up_GB/s": round(up_bytes / t0["up"] / 1e6, 1),
@@ -283,6 +298,8 @@ def sweep(args):
             pt["best_layer_ms"] = round(best[1]["layer"], 5)
             pt["best_up_ms"] = round(best[1]["up"], 5)
             pt["layer_ms_by_block_m"] = by_bm
+            if bm_page in by_bm:
+                pt["page_key_layer_ms"] = by_bm[bm_page]
         print(json.dumps(pt), flush=True)
         rows_md.append(pt)
         del ids, wts
@@ -294,15 +311,17 @@ def sweep(args):
                 ("up roofline frac", "up_roofline_frac"), ("layer ms", "layer_ms"),
                 ("layer TF/s", "layer_TFLOP/s")]
         if cands:
-            cols += [("best bm", "best_block_m"), ("best layer ms", "best_layer_ms")]
-        write_sweep_table(args, base, torch.cuda.get_device_name(dev), cols, rows_md)
+            cols += [("best bm", "best_block_m"), ("best layer ms", "best_layer_ms"),
+                     ("page-key bm", "page_key_block_m"), ("page-key layer ms", "page_key_layer_ms")]
+        write_sweep_table(args, base, torch.cuda.get_device_name(dev), cols, rows_md,
+                          note=SWEEP_KEY_NOTE)
 
 
 def sweep_mx(args, base):
     """The page's own bench: its first expert GEMM alone (MXFP4 weights x e4m3 rows, bias,
     GPT-OSS SwiGLU, e4m3 output) over the 48 batch sizes of one expert-parallel shard.  Per
-    point: moe_align + moe_grouped_gemm_up_mxfp4 at the block size an expert-parallel caller
-    gets from moe_block_m_for(T*k/E_total) (optionally also every --sweep-block-m); TFLOP/s and
+    point: moe_align + moe_grouped_gemm_up_mxfp4 at the shard's block size (shard_block_m;
+    optionally also every --sweep-block-m, and the pages' key T*k/E_total beside it); TFLOP/s and
     TB/s by the page's own counts -- flops 2 * n_slots * H * 2I, bytes = gathered rows + the
     active experts' weights, scales and bias + the e4m3 output."""
     import numpy as np
@@ -356,12 +375,14 @@ def sweep_mx(args, base):
             st = lambda i, j: float(np.mean([e[i].elapsed_time(e[j]) for e in evs]))  # noqa: E731
             return moe.moe_pick_block_m(p), {"align": st(0, 1), "up": st(1, 2)}
 
-        bm_ep = args.block_m or moe.moe_block_m_for(T * K / base.route_experts, "e4m3", "mxfp4")
+        bm_page = moe.moe_block_m_for(T * K / base.route_experts, "e4m3", "mxfp4")
+        bm_ep = args.block_m or shard_block_m(moe, n_loc, active, "e4m3", "mxfp4")
         bm0, t0 = run(bm_ep)
         by_bm = {bm: round(run(bm)[1]["up"], 5) for bm in cands}
         pt = {"sweep": base.name, "T": T, "tokens_per_expert": T * K // base.route_experts,
               "local_slots": n_loc, "active_experts": active, "max_per_expert": int(counts.max()),
-              "block_m": bm0, "align_ms": round(t0["align"], 5), "up_ms": round(t0["up"], 5),
+              "block_m": bm0, "page_key_block_m": bm_page,
+              "align_ms": round(t0["align"], 5), "up_ms": round(t0["up"], 5),
               "up_TFLOP/s": round(flops / t0["up"] / 1e9, 1),
               "up_pct_fp8_peak": round(100 * flops / t0["up"] / 1e9 / peak_tf, 2),
               "up_TB/s": round(nbytes / t0["up"] / 1e9, 3),
@@ -369,6 +390,8 @@ def sweep_mx(args, base):
         if by_bm:
             best = min(by_bm, key=by_bm.get)
             pt.update(best_block_m=best, best_up_ms=by_bm[best], up_ms_by_block_m=by_bm)
+            if bm_page in by_bm:
+                pt["page_key_up_ms"] = by_bm[bm_page]
         print(json.dumps(pt), flush=True)
         rows_md.append(pt)
         del ids
@@ -378,9 +401,11 @@ def sweep_mx(args, base):
                 ("TFLOP/s", "up_TFLOP/s"), ("% fp8 peak", "up_pct_fp8_peak"), ("TB/s", "up_TB/s"),
                 ("roofline frac", "up_roofline_frac")]
         if cands:
-            cols += [("best bm", "best_block_m"), ("best ms", "best_up_ms")]
+            cols += [("best bm", "best_block_m"), ("best ms", "best_up_ms"),
+                     ("page-key bm", "page_key_block_m"), ("page-key ms", "page_key_up_ms")]
         write_sweep_table(args, base, torch.cuda.get_device_name(dev), cols, rows_md,
-                          note=f"  Peak: {peak_tf} TFLOP/s (fp8 MFMA), {PEAK_HBM_GBS / 1000} TB/s.")
+                          note=f"  Peak: {peak_tf} TFLOP/s (fp8 MFMA), {PEAK_HBM_GBS / 1000} TB/s."
+                               + SWEEP_KEY_NOTE)
 
 
 def main():

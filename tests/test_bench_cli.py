@@ -1,5 +1,6 @@
 """bench.py's command-line contract on the host: more than one GPU is refused with a message
-and exit status 2 (this layer runs on one GPU), and --help lists the sweep options."""
+and exit status 2 (this layer runs on one GPU), --help lists the sweep options, and the
+sweep's shard block size follows the shard's own counts."""
 import os
 import subprocess
 import sys
@@ -24,3 +25,18 @@ def test_help_lists_the_modes():
     for opt in ("--sweep", "--sweep-block-m", "--routing", "--graph", "--dense-reference",
                 "--copy-calibration", "--cpu-baseline"):
         assert opt in r.stdout
+
+
+def test_shard_block_m_keys_on_local_counts():
+    """The sweep's shard block size: the block-size rule of the slots a shard received per
+    local expert that received any (a host function; no GPU)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import routed_grouped_gemm_topk_amd as moe
+    # 173 local slots on 10 active experts: 17.3 per expert -> 32-row blocks (the global mean
+    # of the same 128-token batch, 4 per expert, would give 16)
+    assert bench.shard_block_m(moe, 173, 10, "bf16", "bf16") == 32
+    assert moe.moe_block_m_for(128 * 4 / 128, "bf16", "bf16") == 16
+    assert bench.shard_block_m(moe, 0, 0, "bf16", "bf16") == 16           # nothing routed here
+    assert bench.shard_block_m(moe, 41628, 16, "bf16", "bf16") == 256
+    assert bench.shard_block_m(moe, 581, 13, "e4m3", "mxfp4") == 128      # 44.7 per expert
