@@ -165,7 +165,9 @@ def test_mxfp4_problem_validation(lib):
     routing) accept the pair; the MX entry point rejects every other pair."""
     mxp = moe.make_problem(16, 192, 128, 8, 2, "e4m3", "mxfp4")
     assert moe.moe_validate(mxp) == moe.MOE_OK
-    assert moe.moe_pick_block_m(mxp) == moe.moe_block_m_for(4, "e4m3", "mxfp4") == 16
+    assert moe.moe_pick_block_m(mxp) == moe.moe_block_m_for(4, "e4m3", "mxfp4") == 64
+    assert moe.moe_block_m_for(128, "e4m3", "mxfp4") == 64
+    assert moe.moe_block_m_for(128.5, "e4m3", "mxfp4") == 128
     for kw, code in [(dict(block_m=256), moe.MOE_ERR_SHAPE), (dict(H=96), moe.MOE_ERR_SHAPE),
                      (dict(I=96), moe.MOE_ERR_SHAPE)]:
         base = dict(T=16, H=192, I=128, E=8, top_k=2, dtype="e4m3", w_dtype="mxfp4")

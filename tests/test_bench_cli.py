@@ -39,4 +39,5 @@ def test_shard_block_m_keys_on_local_counts():
     assert moe.moe_block_m_for(128 * 4 / 128, "bf16", "bf16") == 16
     assert bench.shard_block_m(moe, 0, 0, "bf16", "bf16") == 16           # nothing routed here
     assert bench.shard_block_m(moe, 41628, 16, "bf16", "bf16") == 256
-    assert bench.shard_block_m(moe, 581, 13, "e4m3", "mxfp4") == 128      # 44.7 per expert
+    assert bench.shard_block_m(moe, 581, 13, "e4m3", "mxfp4") == 64       # 44.7 per expert
+    assert bench.shard_block_m(moe, 41628, 16, "e4m3", "mxfp4") == 128
