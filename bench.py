@@ -28,6 +28,7 @@ METRIC = "fused MoE layer useful TFLOP/s + % MFMA peak (prefill), HBM GB/s (deco
 PEAK_TFLOPS = {"bf16": 2516.6, "e4m3": 5033.2, "f32": 157.3}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "mixtral_prefill_bf16"
+EXTRA_KEY = {"dsv3_decode_bf16": "decode"}   # key of an extra workload's record
 CPU_SAMPLE_TOKENS = {"tiny_fp32": 16, "mixtral_prefill_bf16": 4096, "dsv3_decode_bf16": 16,
                      "skewed_prefill_bf16": 2048, "dsv3_fp8_e4m3": 64}
 
@@ -94,32 +95,46 @@ def measured_traffic(workload: str, stage: str):
         return None
 
 
-def cpu_baseline(case, n_tokens):
-    """Time the CPU oracle (as it stands) on the first n_tokens tokens of the workload."""
-    import numpy as np
+def blas_info():
+    """(library name, threads) of the BLAS numpy calls, from threadpoolctl when present."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            return (f"{blas[0].get('internal_api', '?')} {blas[0].get('version', '')}".strip(),
+                    int(blas[0].get("num_threads", 1)))
+    except Exception:
+        pass
+    return "unknown", int(os.environ.get("OMP_NUM_THREADS", "1"))
 
+
+def cpu_baseline(case, n_tokens):
+    """Time the CPU oracle (as it stands: float64 numpy, BLAS for the per-expert products) on the
+    first n_tokens tokens of the workload.  `cores` is the number of BLAS threads its products
+    run on (the rest of the oracle is single-threaded numpy)."""
     import oracle
     cfg = case.cfg
     toks = list(range(min(n_tokens, cfg.T)))
-    needed = sorted(set(int(e) for e in case.ids_host[toks].reshape(-1)))
+    needed = sorted(set(int(e) for e in case.ids_host[toks].reshape(-1) if 0 <= e < cfg.E))
     log(f"cpu_baseline: fetching {len(needed)} experts to the host")
     host = {e: case.expert_host(e) for e in needed}
     x = case.x_host()
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
-    log(f"cpu_baseline: oracle on {len(toks)} tokens ({threads} BLAS threads)")
+    lib, threads = blas_info()
+    visible = len(os.sched_getaffinity(0))
+    log(f"cpu_baseline: oracle on {len(toks)} tokens ({lib}, {threads} BLAS threads, "
+        f"{visible} host cores visible)")
     t0 = time.perf_counter()
     oracle.moe_layer(x, case.ids_host, case.w_host, lambda e: host[e], cfg.E,
                      fp8=cfg.w_dtype == "e4m3", tokens=toks)
     dt = time.perf_counter() - t0
     flops = 4 * len(toks) * cfg.top_k * cfg.H * cfg.I
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 3),
+            "seconds": round(dt, 3), "host_cores_visible": visible,
+            "blas": {"library": lib, "threads": int(threads)}, "precision": "float64",
             "sample": f"first {len(toks)} of {cfg.T} tokens of {cfg.name} (all their experts), "
-                      f"float64 numpy oracle, weights prefetched to host; useful flops 4*n*k*H*I"}
+                      f"the float64 numpy oracle (per-expert products through BLAS on {threads} "
+                      f"threads, the rest single-threaded), experts in sequence, weights "
+                      f"prefetched to the host and not timed; useful flops 4*n*k*H*I"}
 
 
 def dense_reference(args):
@@ -416,6 +431,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--block-m", type=int, default=0)
+    ap.add_argument("--extra-workloads", default="dsv3_decode_bf16",
+                    help="with the default workload: also time these workloads (comma list, or "
+                         "'none') in the same process and add their records under their keys")
     ap.add_argument("--routing", choices=["on", "off"], default="off",
                     help="on: the step starts from router logits (moe_route_align replaces "
                          "moe_align and produces the ids and weights the GEMMs use)")
@@ -461,15 +479,40 @@ def main():
         sweep(args)
         return
 
-    import routed_grouped_gemm_topk_amd as moe
-    from moe_inputs import CONFIGS, make_case, routing_stats
+    from moe_inputs import CONFIGS
 
-    cfg = CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    res = run_workload(CONFIGS[args.workload], args, dev, cpu_on=args.cpu_baseline == "on",
+                       block_m=args.block_m)
+    extra = [w for w in args.extra_workloads.split(",") if w and w != "none"]
+    if args.workload != DEFAULT_WORKLOAD:
+        extra = []
+    for name in extra:
+        # a second record in the same process, after the headline timing: its layer step, HBM
+        # rate and the up GEMM's roofline; `value` stays the headline workload's
+        torch.cuda.empty_cache()
+        r = run_workload(CONFIGS[name], args, dev, cpu_on=False, block_m=0, routing=False)
+        res[EXTRA_KEY.get(name, name)] = {
+            k: r[k] for k in ("value", "unit", "ms_per_step", "ms_per_step_graph", "config",
+                              "layer_gbps_algorithmic", "kernels", "roofline")}
+        res[EXTRA_KEY.get(name, name)]["pct_hbm_peak_layer"] = round(
+            100 * r["layer_gbps_algorithmic"] / PEAK_HBM_GBS, 2)
+    print(json.dumps(res), flush=True)
+
+
+def run_workload(cfg, args, dev, cpu_on, block_m=0, routing=None):
+    """Time one workload's step (staged entry points with HIP events, graph replay,
+    moe_forward) and return its result record."""
+    import numpy as np
+    import torch
+
+    import routed_grouped_gemm_topk_amd as moe
+    from moe_inputs import make_case, routing_stats
+
     log(f"generating {cfg.name} on {torch.cuda.get_device_name(dev)}")
     case = make_case(cfg, dev, seed=0)
-    p = moe.make_problem(cfg.T, cfg.H, cfg.I, cfg.E, cfg.top_k, cfg.x_dtype, cfg.w_dtype, args.block_m)
+    p = moe.make_problem(cfg.T, cfg.H, cfg.I, cfg.E, cfg.top_k, cfg.x_dtype, cfg.w_dtype, block_m)
     bm = moe.moe_pick_block_m(p)
     rows, mt = moe.moe_max_padded_slots(p), moe.moe_max_tiles(p)
     fp8 = cfg.w_dtype == "e4m3"
@@ -482,7 +525,7 @@ def main():
     out = torch.empty((cfg.T, cfg.H), dtype=case.x.dtype, device=dev)
     ws = moe.alloc_workspace(p, dev)
     gemm_ws = moe.alloc_gemm_workspace(p, dev)
-    routing = args.routing == "on"
+    routing = (args.routing == "on") if routing is None else routing
     if routing:
         from moe_inputs import make_logits
         logits = torch.from_numpy(make_logits(cfg, 0).astype(np.float32)).to(dev)
@@ -636,7 +679,7 @@ def main():
         per_kernel[s] = d
 
     cpu = None
-    if args.cpu_baseline == "on":
+    if cpu_on:
         cpu = cpu_baseline(case, CPU_SAMPLE_TOKENS.get(cfg.name, 64))
         if unit == "GB/s":
             cpu["note"] = "reported in TFLOP/s (useful flops); the GPU value is GB/s"
@@ -670,7 +713,9 @@ def main():
     }
     if routing_cmp:
         res["routing"] = routing_cmp
-    print(json.dumps(res), flush=True)
+    del case
+    return res
+
 
 
 if __name__ == "__main__":

@@ -104,27 +104,37 @@ int moe_validate(const moe_problem* p);
 
 /* Rows per m-block the library uses for `p` (p->block_m if non-zero, else
  * moe_block_m_for(T*top_k/E, dtype, w_dtype)).  Returns a negative moe_status
- * for an invalid problem. */
+ * for an invalid problem.  Block size by expected slice size: "MOE Bmm1 Fused
+ * Gather", _select_base_config. */
 int32_t moe_pick_block_m(const moe_problem* p);
 
 /* The library's block size for `slots_per_expert` expected slots per expert, in
  * the manner of the block-size table of "MOE Bmm1 Fused Gather"
  * (_select_base_config, keyed on the expected slice size): few slots per expert
- * -> small blocks.  moe_pick_block_m assumes every id is a local expert; a
+ * -> small blocks.  moe_pick_block_m assumes every id is a local expert.  A
  * caller whose ids mostly belong to other shards (expert parallelism: E local of
- * E_total experts) passes T*top_k/E_total here and sets block_m to the result.
+ * E_total experts) passes the slots it received per local expert that received
+ * any (from its dispatch counts) and sets block_m to the result: a shard holding
+ * popular experts receives several times the global mean.  (The page's bench keys
+ * the same choice on the global mean T*top_k/E_total.)
  * Host only, no side effects.  MOE_ERR_DTYPE for an unsupported dtype pair,
  * MOE_ERR_SHAPE for a negative or NaN count. */
 int32_t moe_block_m_for(double slots_per_expert, int32_t dtype, int32_t w_dtype);
 
+/* Size queries (library utilities; the pages define no such calls).  They let the
+ * caller allocate the outputs of moe_align and the workspaces before any launch, so
+ * that no entry point needs the device-side counts on the host. */
+
 /* Upper bound on rows of the padded expert-sorted slot list:
- * N + min(E, N) * (block_m - 1).  Negative moe_status if invalid. */
+ * N + min(E, N) * (block_m - 1) (each of at most min(E, N) non-empty experts pads
+ * fewer than block_m rows).  Negative moe_status if invalid. */
 int64_t moe_max_padded_slots(const moe_problem* p);
 
 /* Upper bound on m-blocks (tiles): moe_max_padded_slots / block_m. */
 int64_t moe_max_tiles(const moe_problem* p);
 
-/* Bytes of device workspace moe_forward needs (256-byte aligned pieces). */
+/* Bytes of device workspace moe_forward needs (256-byte aligned pieces).  Library
+ * utility, no page. */
 int64_t moe_workspace_bytes(const moe_problem* p);
 
 /*
@@ -265,7 +275,8 @@ int moe_grouped_gemm_down(const moe_problem* p, const void* act, const float* ac
 
 /*
  * Bytes of the optional workspace of moe_grouped_gemm_up and moe_grouped_gemm_down (0: the
- * problem's GEMMs never use one); negative moe_status for an invalid problem.
+ * problem's GEMMs never use one); negative moe_status for an invalid problem.  Library
+ * utility, no page (the split it sizes is this library's own, see below).
  * The workspace is device memory, 256-byte aligned, caller-owned scratch whose contents are
  * unspecified afterwards; calls that share one must not overlap.  With it, bf16 problems of
  * 128- or 256-row m-blocks cut the tiles of a GEMM's last, partly filled round of workgroups

@@ -310,7 +310,7 @@ ExpertGetter = Callable[[int], tuple]
 
 def moe_layer(x, topk_ids, topk_weights, experts, num_experts: Optional[int] = None, *,
               fp8: bool = False, group: int = 128, tokens: Optional[Sequence[int]] = None,
-              return_slots: bool = False):
+              return_slots: bool = False, workers: int = 1):
     """out[t] = sum_j w[t,j] * W2[e] (SiLU(W13g[e] x_t) * W13u[e] x_t), e = ids[t,j].
 
     Per active expert: gather the expert's slots' token rows (token = slot // k),
@@ -324,6 +324,9 @@ def moe_layer(x, topk_ids, topk_weights, experts, num_experts: Optional[int] = N
     fp8: X and the intermediate activation go through per-(row, group)
       e4m3 quantisation (see module docstring); weights are dequantised codes.
     tokens: compute only these token rows (the returned rows follow this order).
+    workers: experts are independent of each other, so with workers > 1 they are
+      evaluated by that many threads at once; each expert's arithmetic and the
+      combine order are the same, so the result is identical bit for bit.
     Returns out [len(tokens), H] float64 (and the per-slot rows if asked).
     """
     x = np.asarray(x)
@@ -349,11 +352,11 @@ def moe_layer(x, topk_ids, topk_weights, experts, num_experts: Optional[int] = N
 
     toks = list(range(T)) if tokens is None else [int(t) for t in tokens]
     slots = [t * k + j for t in toks for j in range(k)]
-    slot_vals = {}
-    for e in range(E):
+    def one_expert(e):
+        """Rows w[s] * W2[e] act(x_{s//k}) of expert e's slots s (ascending s)."""
         mine = [s for s in slots if int(ids.flat[s]) == e]
         if not mine:
-            continue
+            return {}
         w13_e, w2_e, s13_e, s2_e = get(e)
         if fp8:
             w13_e = dequantize_blocks(w13_e, s13_e, group)
@@ -364,8 +367,17 @@ def moe_layer(x, topk_ids, topk_weights, experts, num_experts: Optional[int] = N
             aq, sa = quantize_groups_e4m3(act.astype(np.float32), group)
             act = dequantize_groups(aq, sa, group)
         y = expert_down(act, w2_e)
-        for i, s in enumerate(mine):
-            slot_vals[s] = wts.flat[s] * y[i]
+        return {s: wts.flat[s] * y[i] for i, s in enumerate(mine)}
+
+    slot_vals = {}
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=int(workers)) as ex:
+            for part in ex.map(one_expert, range(E)):
+                slot_vals.update(part)
+    else:
+        for e in range(E):
+            slot_vals.update(one_expert(e))
 
     zero = np.zeros(H, dtype=np.float64)
     slot_rows = np.stack([slot_vals.get(s, zero) for s in slots]) if slots else np.zeros((0, H))

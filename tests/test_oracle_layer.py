@@ -198,3 +198,24 @@ def test_fp8_layer_vs_torch_quantisation_chain():
             a = tq(a.numpy())
             ref[t] += float(case.w_host[t, j]) * F.linear(a, W2[e])[0]
     np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_expert_threads_bit_identical(fp8):
+    """Evaluating the experts on several threads changes nothing: each expert's arithmetic
+    and the combine order are the same."""
+    rng = np.random.default_rng(31)
+    T, H, I, E, k = 37, 256, 128, 9, 3
+    x, ids, w, w13, w2 = rand_problem(rng, T, H, I, E, k, distinct=False)
+    ids[5, 1] = E                       # an excluded id
+    if fp8:
+        c13 = rng.integers(0, 126, (E, 2 * I, H)).astype(np.uint8)
+        c2 = rng.integers(0, 126, (E, H, I)).astype(np.uint8)
+        s13 = rng.uniform(1e-3, 1e-2, (E, 2 * I // 128, H // 128))
+        s2 = rng.uniform(1e-3, 1e-2, (E, H // 128, I // 128))
+        experts = (c13, c2, s13, s2)
+    else:
+        experts = (w13, w2)
+    one, slots1 = oracle.moe_layer(x, ids, w, experts, E, fp8=fp8, return_slots=True)
+    many, slots8 = oracle.moe_layer(x, ids, w, experts, E, fp8=fp8, return_slots=True, workers=8)
+    assert np.array_equal(one, many) and np.array_equal(slots1, slots8)
