@@ -314,6 +314,35 @@ int moe_forward(const moe_problem* p, const void* x, const int32_t* topk_ids,
                 const void* w2, const float* w2_scales, void* out, void* workspace,
                 size_t workspace_bytes, void* stream);
 
+/*
+ * Bytes of the library-owned device array behind moe_forward_scratch (one per GPU the
+ * library runs on, held until the process ends).
+ */
+#define MOE_SCRATCH_MAX_BYTES (128u * 1024u * 1024u)
+
+/* MOE_SCRATCH_MAX_BYTES as a value (host only). */
+int64_t moe_scratch_max_bytes(void);
+
+/*
+ * moe_forward_scratch -- moe_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, kernels, launch sequence and results (bit for bit) as moe_forward, but the
+ * intermediates live in a library-owned device array of MOE_SCRATCH_MAX_BYTES on the current
+ * GPU instead of a caller workspace.  The call allocates nothing (no hipMalloc, no allocating
+ * library routine); the caller still passes every input and `out`.
+ * n_invalid: NULL, or device int32 [1] that receives the number of excluded slots.
+ * Errors: MOE_ERR_WORKSPACE when moe_workspace_bytes(p) exceeds MOE_SCRATCH_MAX_BYTES (the
+ * problem does not fit: use moe_forward); MOE_ERR_DEVICE if the array's address cannot be
+ * obtained; otherwise as moe_forward.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's contents (no part
+ * of it needs to start zeroed).  Calls that overlap on one GPU -- on different streams, or
+ * from different threads without ordering -- race on it and give undefined results.
+ */
+int moe_forward_scratch(const moe_problem* p, const void* x, const int32_t* topk_ids,
+                        const float* topk_weights, const void* w13, const float* w13_scales,
+                        const void* w2, const float* w2_scales, void* out, int32_t* n_invalid,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,6 +35,7 @@ from ._lib import (  # noqa: F401
     moe_combine,
     moe_gemm_workspace_bytes,
     moe_forward,
+    moe_forward_scratch,
     moe_grouped_gemm_down,
     moe_grouped_gemm_up,
     moe_grouped_gemm_up_mxfp4,
@@ -44,6 +45,7 @@ from ._lib import (  # noqa: F401
     moe_quantize_rows_e4m3,
     moe_route,
     moe_route_align,
+    moe_scratch_max_bytes,
     moe_validate,
     moe_workspace_bytes,
     status_str,

@@ -34,7 +34,7 @@ EXPORTS = ["moe_status_str", "moe_validate", "moe_pick_block_m", "moe_block_m_fo
            "moe_max_tiles", "moe_workspace_bytes", "moe_route", "moe_route_align", "moe_align",
            "moe_quantize_rows_e4m3", "moe_grouped_gemm_up", "moe_grouped_gemm_up_mxfp4",
            "moe_grouped_gemm_down", "moe_gemm_workspace_bytes",
-           "moe_combine", "moe_forward"]
+           "moe_combine", "moe_forward", "moe_scratch_max_bytes", "moe_forward_scratch"]
 
 
 class MoeError(RuntimeError):
@@ -95,6 +95,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "moe_gemm_workspace_bytes": (ctypes.c_int64, [P]),
         "moe_combine": (ctypes.c_int, [P, vp, vp, vp, vp]),
         "moe_forward": (ctypes.c_int, [P] + [vp] * 9 + [ctypes.c_size_t, vp]),
+        "moe_scratch_max_bytes": (ctypes.c_int64, []),
+        "moe_forward_scratch": (ctypes.c_int, [P] + [vp] * 9 + [vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -316,3 +318,22 @@ def moe_forward(p: Problem, x, topk_ids, topk_weights, w13, w13_scales, w2, w2_s
             _ptr(workspace, "workspace")]
     _checked(load().moe_forward(ctypes.byref(p), *args, ctypes.c_size_t(ws_bytes), _stream(stream)),
              "moe_forward")
+
+
+def moe_scratch_max_bytes() -> int:
+    return int(load().moe_scratch_max_bytes())
+
+
+def moe_forward_scratch(p: Problem, x, topk_ids, topk_weights, w13, w13_scales, w2, w2_scales,
+                        out, n_invalid=None, stream=None) -> None:
+    args = [_ptr(x, "x", _TORCH_DT[p.dtype], p.T * p.H),
+            _ptr(topk_ids, "topk_ids", torch.int32, p.T * p.top_k),
+            _ptr(topk_weights, "topk_weights", torch.float32, p.T * p.top_k),
+            _ptr(w13, "w13", _w_dtype(p), p.E * 2 * p.I * p.H),
+            _ptr(w13_scales, "w13_scales", torch.float32, p.E * (2 * p.I // 128) * (p.H // 128)),
+            _ptr(w2, "w2", _w_dtype(p), p.E * p.H * p.I),
+            _ptr(w2_scales, "w2_scales", torch.float32, p.E * (p.H // 128) * (p.I // 128)),
+            _ptr(out, "out", _TORCH_DT[p.dtype], p.T * p.H),
+            _ptr(n_invalid, "n_invalid", torch.int32, 1)]
+    _checked(load().moe_forward_scratch(ctypes.byref(p), *args, _stream(stream)),
+             "moe_forward_scratch")

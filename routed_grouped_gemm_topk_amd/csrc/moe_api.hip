@@ -126,6 +126,13 @@ std::mutex g_dev_mu;
 int8_t g_dev_ok[64];      // 0 unknown, 1 ok, -1 not gfx950
 int g_dev_cus[64];        // compute units, 0 until known
 
+// Library-owned intermediates of moe_forward_scratch: one copy per device, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the device array, so
+// host code never passes it to a kernel or a copy; it uses the device address that
+// hipGetSymbolAddress returns for the current device (g_scratch_ptr).
+static __device__ __align__(256) char scratch[MOE_SCRATCH_MAX_BYTES];
+char* g_scratch_ptr[64];  // device address of `scratch` per device ordinal, null until known
+
 // gfx950 check, cached per device ordinal (with the device's compute-unit count).
 int check_device() {
   int dev = 0;
@@ -142,6 +149,20 @@ int check_device() {
 
 int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
 
+// Device address of this device's `scratch`, looked up once per device with that device
+// current (each device holds its own copy at its own address).  Null on failure.
+char* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> g(g_dev_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = (char*)p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 // MOE_ERR_ALIGN unless every non-null pointer is aligned to its byte count.
 struct Al {
   const void* p;
@@ -151,6 +172,45 @@ int check_align(std::initializer_list<Al> ptrs) {
   for (const Al& x : ptrs)
     if (x.p && ((uintptr_t)x.p & (uintptr_t)(x.a - 1))) return MOE_ERR_ALIGN;
   return MOE_OK;
+}
+
+// The launch sequence of moe_forward in the workspace `ws` (device memory of at least
+// L.total bytes, 256-byte aligned); n_invalid: where the excluded-slot count goes (null: the
+// workspace's first int32).  No piece of the workspace needs to start zeroed: every one is
+// written before it is read in the same call.
+int forward_in(const Resolved& r, const Layout& L, char* ws, int32_t* n_invalid, const void* x,
+               const int32_t* topk_ids, const float* topk_weights, const void* w13,
+               const float* w13_scales, const void* w2, const float* w2_scales, void* out,
+               hipStream_t s) {
+  const bool fp8 = r.w_dtype == MOE_E4M3;
+  auto at = [&](int64_t off) { return off < 0 ? nullptr : (void*)(ws + off); };
+  if (!n_invalid) n_invalid = (int32_t*)at(L.status);
+  int32_t* counts = (int32_t*)at(L.counts);
+  int32_t* offsets = (int32_t*)at(L.offsets);
+  int32_t* sorted_slots = (int32_t*)at(L.sorted_slots);
+  int32_t* slot_row = (int32_t*)at(L.slot_row);
+  int32_t* tiles = (int32_t*)at(L.tiles);
+  int32_t* num_tiles = (int32_t*)at(L.num_tiles);
+
+  hipError_t e = launch_align(r, topk_ids, counts, offsets, sorted_slots, slot_row, tiles,
+                              num_tiles, n_invalid, s);
+  if (e != hipSuccess) return MOE_ERR_LAUNCH;
+  const void* x_in = x;
+  const float* x_scales = nullptr;
+  if (fp8) {
+    e = launch_quant_rows(r, x, (uint8_t*)at(L.xq), (float*)at(L.x_scales), s);
+    if (e != hipSuccess) return MOE_ERR_LAUNCH;
+    x_in = at(L.xq);
+    x_scales = (const float*)at(L.x_scales);
+  }
+  e = launch_up(r, x_in, x_scales, w13, w13_scales, sorted_slots, offsets, tiles, num_tiles,
+                at(L.act), (float*)at(L.act_scales), at(L.split), s);
+  if (e != hipSuccess) return MOE_ERR_LAUNCH;
+  e = launch_down(r, at(L.act), (const float*)at(L.act_scales), w2, w2_scales, topk_weights,
+                  sorted_slots, offsets, tiles, num_tiles, at(L.slot_out), at(L.split), s);
+  if (e != hipSuccess) return MOE_ERR_LAUNCH;
+  e = launch_combine(r, at(L.slot_out), slot_row, out, s);
+  return status_of(e);
 }
 
 }  // namespace
@@ -379,37 +439,33 @@ int moe_forward(const moe_problem* p, const void* x, const int32_t* topk_ids,
                         {w2, 16}, {w2_scales, 4}, {out, 16}, {workspace, 256}})))
     return v;
   if ((v = check_device())) return v;
-
-  char* ws = (char*)workspace;
-  auto at = [&](int64_t off) { return off < 0 ? nullptr : (void*)(ws + off); };
-  int32_t* n_invalid = (int32_t*)at(L.status);
-  int32_t* counts = (int32_t*)at(L.counts);
-  int32_t* offsets = (int32_t*)at(L.offsets);
-  int32_t* sorted_slots = (int32_t*)at(L.sorted_slots);
-  int32_t* slot_row = (int32_t*)at(L.slot_row);
-  int32_t* tiles = (int32_t*)at(L.tiles);
-  int32_t* num_tiles = (int32_t*)at(L.num_tiles);
-  hipStream_t s = (hipStream_t)stream;
-
-  hipError_t e = launch_align(r, topk_ids, counts, offsets, sorted_slots, slot_row, tiles,
-                              num_tiles, n_invalid, s);
-  if (e != hipSuccess) return MOE_ERR_LAUNCH;
-  const void* x_in = x;
-  const float* x_scales = nullptr;
-  if (fp8) {
-    e = launch_quant_rows(r, x, (uint8_t*)at(L.xq), (float*)at(L.x_scales), s);
-    if (e != hipSuccess) return MOE_ERR_LAUNCH;
-    x_in = at(L.xq);
-    x_scales = (const float*)at(L.x_scales);
-  }
-  e = launch_up(r, x_in, x_scales, w13, w13_scales, sorted_slots, offsets, tiles, num_tiles,
-                at(L.act), (float*)at(L.act_scales), at(L.split), s);
-  if (e != hipSuccess) return MOE_ERR_LAUNCH;
-  e = launch_down(r, at(L.act), (const float*)at(L.act_scales), w2, w2_scales, topk_weights,
-                  sorted_slots, offsets, tiles, num_tiles, at(L.slot_out), at(L.split), s);
-  if (e != hipSuccess) return MOE_ERR_LAUNCH;
-  e = launch_combine(r, at(L.slot_out), slot_row, out, s);
-  return status_of(e);
+  return forward_in(r, L, (char*)workspace, nullptr, x, topk_ids, topk_weights, w13, w13_scales,
+                    w2, w2_scales, out, (hipStream_t)stream);
 }
+
+int moe_forward_scratch(const moe_problem* p, const void* x, const int32_t* topk_ids,
+                        const float* topk_weights, const void* w13, const float* w13_scales,
+                        const void* w2, const float* w2_scales, void* out, int32_t* n_invalid,
+                        void* stream) {
+  int v = validate(p);
+  if (v) return v;
+  if (is_mx(p)) return MOE_ERR_DTYPE;
+  if (!x || !topk_ids || !topk_weights || !w13 || !w2 || !out) return MOE_ERR_NULL;
+  const bool fp8 = p->w_dtype == MOE_E4M3;
+  if (fp8 && (!w13_scales || !w2_scales)) return MOE_ERR_NULL;
+  const Resolved r = resolve(p);
+  const Layout L = layout(r);
+  if (L.total > (int64_t)MOE_SCRATCH_MAX_BYTES) return MOE_ERR_WORKSPACE;
+  if ((v = check_align({{x, 16}, {topk_ids, 4}, {topk_weights, 4}, {w13, 16}, {w13_scales, 4},
+                        {w2, 16}, {w2_scales, 4}, {out, 16}, {n_invalid, 4}})))
+    return v;
+  if ((v = check_device())) return v;
+  char* ws = scratch_ptr();
+  if (!ws) return MOE_ERR_DEVICE;
+  return forward_in(r, L, ws, n_invalid, x, topk_ids, topk_weights, w13, w13_scales, w2,
+                    w2_scales, out, (hipStream_t)stream);
+}
+
+int64_t moe_scratch_max_bytes(void) { return (int64_t)MOE_SCRATCH_MAX_BYTES; }
 
 }  // extern "C"

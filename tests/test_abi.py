@@ -252,3 +252,23 @@ def test_gemm_workspace_size_and_checks(lib):
                                    None) == W
     assert lib.moe_grouped_gemm_up(P, ok, None, ok, None, ok, ok, ok, ok, ok, None, odd, need,
                                    None) == A
+
+
+def test_forward_scratch_host_checks(lib):
+    """moe_forward_scratch: validation before any HIP call -- null pointers, and a problem whose
+    intermediates exceed the library-owned array (MOE_SCRATCH_MAX_BYTES) is refused."""
+    assert moe.moe_scratch_max_bytes() == 128 << 20
+    fake = 1 << 20                                   # never dereferenced
+    small = moe.make_problem(64, 512, 256, 16, 4, "bf16")
+    assert lib.moe_forward_scratch(ctypes.byref(small), None, fake, fake, fake, None, fake, None,
+                                   fake, None, None) == moe.MOE_ERR_NULL
+    big = moe.make_problem(4096, 4096, 14336, 8, 2, "bf16")
+    assert moe.moe_workspace_bytes(big) > moe.moe_scratch_max_bytes()
+    assert lib.moe_forward_scratch(ctypes.byref(big), fake, fake, fake, fake, None, fake, None,
+                                   fake, None, None) == moe.MOE_ERR_WORKSPACE
+    mx = moe.make_problem(64, 512, 256, 16, 4, "e4m3", "mxfp4")
+    assert lib.moe_forward_scratch(ctypes.byref(mx), fake, fake, fake, fake, None, fake, None,
+                                   fake, None, None) == moe.MOE_ERR_DTYPE
+    odd = moe.make_problem(64, 512, 256, 16, 4, "bf16")
+    assert lib.moe_forward_scratch(ctypes.byref(odd), fake + 8, fake, fake, fake, None, fake, None,
+                                   fake, None, None) == moe.MOE_ERR_ALIGN
