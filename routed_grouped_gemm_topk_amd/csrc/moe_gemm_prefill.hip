@@ -93,6 +93,25 @@ __device__ __forceinline__ TailSplit tail_split(int total, int slots, int kt_all
   return t;
 }
 
+// Raw buffer descriptor of [base, base + bytes): 32-bit offsets, no stride; a lane whose offset
+// is past `bytes` reads zeros without touching memory.
+__device__ __forceinline__ i32x4 buf_rsrc(const void* base, uint32_t bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));   // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);                 // num_records (bytes)
+  r[3] = 0x00020000;                                                 // raw 32-bit data
+  return r;
+}
+
+// 64 lanes x 16 bytes from the buffer at voff + soff straight to LDS at M0 (MUBUF
+// buffer_load_dwordx4 ... lds).
+__device__ __forceinline__ void buf_dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               ::"v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory");
+}
+
 // ---------------------------------------------------------------------------------------------
 // Direct-to-LDS variant: the global -> LDS copies are global_load_lds_dwordx4 (each wave
 // instruction lands 64 x 16 bytes contiguously in LDS at M0), so no registers stage the
@@ -102,7 +121,13 @@ __device__ __forceinline__ TailSplit tail_split(int total, int slots, int kt_all
 // ring each k-slice.  The per-lane source address is chosen so that the fixed
 // lane -> LDS position mapping realises the XOR swizzle above.
 // ---------------------------------------------------------------------------------------------
-template <int BMT, int BK, int NS, int BNA, bool UP, int WM, int WN>
+// BUF: the copies are MUBUF buffer_load_dwordx4 ... lds against one buffer descriptor per wave
+// (its copies are all gathered/act rows or all weight rows): 32-bit offsets instead of 64-bit
+// addresses per lane (24 fewer VGPRs at 256-row blocks), the k offset in the scalar soffset,
+// and padding rows of the gathered operand at an offset past the end of X, read as zeros
+// without a memory access.  Measured against the global_load_lds form on the Mixtral-shaped
+// workload: 2% faster, bit-identical.
+template <int BMT, int BK, int NS, int BNA, bool UP, int WM, int WN, bool BUF = false>
 __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
   constexpr int ROWB = BK * 2, KK = BK / 16, NW = WN * WM;
   constexpr int BROWS = UP ? 2 * BNA : BNA;
@@ -122,7 +147,7 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wn = wave % WN;
   const int wm = wave / WN;
   const int mrow0 = wm * (BMT / WM);               // this wave's first row of the m-block
@@ -151,9 +176,23 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
   const int K = g.K;
   const int KT = kend - kbeg;                       // k-slices of this workgroup, from kbeg
 
-  // ---- this wave's copies: source row pointers (k-slice 0) and LDS offsets -----------------
-  const char* src[NQW];
+  // ---- this wave's copies: source of each row chunk (k-slice 0) and LDS offsets -----------
+  // FLAT: a 64-bit address per copy; BUF: a 32-bit offset into this wave's buffer (X or the
+  // m-block's act rows for A copies, the expert's weight slab for weight copies).
+  static_assert(!BUF || BMT % (NQW * ROWS_PER_Q) == 0, "BUF: a wave copies only A or only weight rows");
   const char* wbase = g.w + (size_t)e * g.w_expert_elems * 2;
+  const bool a_wave = wave * NQW * ROWS_PER_Q < BMT;
+  i32x4 rsrc{};
+  if (BUF) {
+    if (!a_wave)
+      rsrc = buf_rsrc(wbase, (uint32_t)(g.w_expert_elems * 2));
+    else if (UP)
+      rsrc = buf_rsrc(g.a_src, (uint32_t)((size_t)(g.n_slots / g.top_k) * K * 2));
+    else
+      rsrc = buf_rsrc(g.a_src + (size_t)row0 * K * 2, (uint32_t)(BMT * K * 2));
+  }
+  const char* src[BUF ? 1 : NQW];
+  uint32_t voff[BUF ? NQW : 1];
   #pragma unroll
   for (int i = 0; i < NQW; ++i) {
     const int q = wave * NQW + i;
@@ -162,10 +201,14 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
     if (r < BMT) {
       if (UP) {
         const int s = g.sorted_slots[row0 + r];
-        src[i] = (s < g.n_slots) ? g.a_src + (size_t)(s / g.top_k) * K * 2 + cc * 16
-                                 : g_zero_row + cc * 16;
+        if constexpr (BUF)
+          voff[i] = (s < g.n_slots) ? (uint32_t)((s / g.top_k) * K * 2 + cc * 16) : 0x80000000u;
+        else
+          src[i] = (s < g.n_slots) ? g.a_src + (size_t)(s / g.top_k) * K * 2 + cc * 16
+                                   : g_zero_row + cc * 16;
       } else {
-        src[i] = g.a_src + (size_t)(row0 + r) * K * 2 + cc * 16;
+        if constexpr (BUF) voff[i] = (uint32_t)(r * K * 2 + cc * 16);
+        else src[i] = g.a_src + (size_t)(row0 + r) * K * 2 + cc * 16;
       }
     } else {
       // weight row; past n_out (ragged last n-block) the last row is re-read, its products
@@ -173,7 +216,8 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
       const int rb = r - BMT;
       const int nr = min(n0 + (UP && rb >= BNA ? rb - BNA : rb), g.n_out - 1);
       const int grow = (UP && rb >= BNA) ? g.n_out + nr : nr;
-      src[i] = wbase + (size_t)grow * K * 2 + cc * 16;
+      if constexpr (BUF) voff[i] = (uint32_t)(grow * K * 2 + cc * 16);
+      else src[i] = wbase + (size_t)grow * K * 2 + cc * 16;
     }
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
@@ -181,7 +225,10 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
     const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + buf * STAGE + wave * NQW * 1024);
     const int koff = kt * ROWB;
     #pragma unroll
-    for (int i = 0; i < NQW; ++i) lds_dma16(src[i] + koff, st + i * 1024);
+    for (int i = 0; i < NQW; ++i) {
+      if constexpr (BUF) buf_dma16(rsrc, voff[i], (uint32_t)koff, st + i * 1024);
+      else lds_dma16(src[i] + koff, st + i * 1024);
+    }
   };
 
   // ---- fragments -----------------------------------------------------------------------------
@@ -436,7 +483,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(Args g) {
   }
 }
 
-template <int BK, int NS, int BNA, bool UP, int WM = 1, int BMT = BM, int WN = 4>
+template <int BK, int NS, int BNA, bool UP, int WM = 1, int BMT = BM, int WN = 4, bool BUF = false>
 hipError_t run_dma(Args a, hipStream_t s) {
   // sized by the host-side tile bound; blocks past the device-side tile count exit at once
   const int64_t grid = xcd_chunked_grid<kChunk>((int64_t)a.tiles_max * ((a.n_out + BNA - 1) / BNA));
@@ -445,7 +492,7 @@ hipError_t run_dma(Args a, hipStream_t s) {
   if (!split) a.slots = 0;
   static_assert(BK == kSplitBK, "the K-split tail assumes 64-wide k-slices");
   a.grid_tiles = (int)grid;
-  hipLaunchKernelGGL((gemm_dma_kernel<BMT, BK, NS, BNA, UP, WM, WN>),
+  hipLaunchKernelGGL((gemm_dma_kernel<BMT, BK, NS, BNA, UP, WM, WN, BUF>),
                      dim3((unsigned)(grid + (split ? a.slots : 0))), dim3(WN * WM * kWave), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
@@ -494,7 +541,12 @@ hipError_t launch_up_prefill(const Resolved& r, const void* x, const void* w13,
   a.w_expert_elems = (int64_t)2 * r.I * r.H;
   // 256-row m-blocks: 8 waves, 4 along M (64 rows each) x 2 along N.  I a multiple of 64
   // but not of 128: the last 128-wide n-block is half used.
-  if (r.BM == 256) return pf::run_dma<64, 2, 128, true, 4, 256, 2>(a, s);
+  // MUBUF copies need X's byte size below 2^31 (32-bit offsets; padding at 2^31 reads zeros)
+  if (r.BM == 256) {
+    if ((int64_t)r.T * r.H * 2 < ((int64_t)1 << 31))
+      return pf::run_dma<64, 2, 128, true, 4, 256, 2, true>(a, s);
+    return pf::run_dma<64, 2, 128, true, 4, 256, 2>(a, s);
+  }
   if (r.I % 256 == 0) return pf::run_dma<64, 2, 256, true, 2>(a, s);
   return pf::run_dma<64, 3, 128, true>(a, s);
 }
@@ -523,7 +575,7 @@ hipError_t launch_down_prefill(const Resolved& r, const void* act, const void* w
   a.w_expert_elems = (int64_t)r.H * r.I;
   // H a multiple of 64 but not of 128: the last 128-wide n-block is half used
   if (r.BM == 256) {
-    if (r.H % 256 == 0) return pf::run_dma<64, 2, 256, false, 4, 256, 2>(a, s);
+    if (r.H % 256 == 0) return pf::run_dma<64, 2, 256, false, 4, 256, 2, true>(a, s);
     return pf::run_dma<64, 2, 128, false, 4, 256, 2>(a, s);
   }
   if (r.H % 256 == 0) return pf::run_dma<64, 3, 256, false, 2>(a, s);
