@@ -102,11 +102,10 @@ __global__ __launch_bounds__(WN * WM * kWave) void mx_up_kernel(Args g) {
   const int nblk = g.I / BNA;
   const int logical = xcd_logical(blockIdx.x, ntiles * nblk);
   if (logical < 0) return;
-  int mt, nt;
-  grouped_tile<BM, kGroupM>(logical, nblk, g.tiles, g.offsets, mt, nt);
-  const int e = g.tiles[2 * mt];
-  const int row0 = g.tiles[2 * mt + 1];
-  const int n0 = nt * BNA;                         // first act column; weight rows from 2*n0
+  const TileRef tr = grouped_tile<BM, kGroupM>(logical, nblk, g.tiles, g.offsets);
+  const int e = tr.e;
+  const int row0 = tr.row0;
+  const int n0 = tr.nt * BNA;                         // first act column; weight rows from 2*n0
   const int K = g.K;
   const int KT = (K + KS - 1) / KS;
   const int KB = K / 32;                           // microscale blocks per row

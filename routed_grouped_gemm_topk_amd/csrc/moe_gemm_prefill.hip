@@ -168,11 +168,10 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
     kend = (part + 1) * KT_all / ts.S;
     unit = ti * ts.S + part;
   }
-  int mt, nt;
-  grouped_tile<BMT, GROUP_M>(logical, nblk, g.tiles, g.offsets, mt, nt);
-  const int e = g.tiles[2 * mt];
-  const int row0 = g.tiles[2 * mt + 1];
-  const int n0 = nt * BNA;
+  const TileRef tr = grouped_tile<BMT, GROUP_M>(logical, nblk, g.tiles, g.offsets);
+  const int e = tr.e;
+  const int row0 = tr.row0;
+  const int n0 = tr.nt * BNA;
   const int K = g.K;
   const int KT = kend - kbeg;                       // k-slices of this workgroup, from kbeg
 
@@ -435,10 +434,9 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(Args g) {
   const TailSplit ts = tail_split(*g.num_tiles * nblk, g.slots, g.K / kSplitBK);
   const int ti = (int)blockIdx.x / (BMT / RPB);
   if (ti >= ts.r) return;
-  int mt, nt;
-  grouped_tile<BMT, GROUP_M>(ts.full + ti, nblk, g.tiles, g.offsets, mt, nt);
-  const int row0 = g.tiles[2 * mt + 1];
-  const int n0 = nt * BNA;
+  const TileRef tr = grouped_tile<BMT, GROUP_M>(ts.full + ti, nblk, g.tiles, g.offsets);
+  const int row0 = tr.row0;
+  const int n0 = tr.nt * BNA;
   const int lane = threadIdx.x & (kWave - 1);
   const int c0 = lane * CPL;
   const size_t pstride = (size_t)BMT * PW;

@@ -100,11 +100,10 @@ __global__ __launch_bounds__(WN * WM * kWave) void stream_kernel(Args g) {
   const int nblk = g.n_out / BNA;
   const int logical = xcd_logical(blockIdx.x, ntiles * nblk);
   if (logical < 0) return;
-  int mt, nt;
-  grouped_tile<BM, kGroupM>(logical, nblk, g.tiles, g.offsets, mt, nt);
-  const int e = g.tiles[2 * mt];
-  const int row0 = g.tiles[2 * mt + 1];
-  const int n0 = nt * BNA;
+  const TileRef tr = grouped_tile<BM, kGroupM>(logical, nblk, g.tiles, g.offsets);
+  const int e = tr.e;
+  const int row0 = tr.row0;
+  const int n0 = tr.nt * BNA;
   const int K = g.K;
   const int KT = K / BK;
   const int KB = K / kGroup;                    // scale blocks along K (e4m3)
@@ -202,6 +201,7 @@ __global__ __launch_bounds__(WN * WM * kWave) void stream_kernel(Args g) {
     #pragma unroll
     for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  int fmv = FM;                                 // 16-row fragments holding valid rows (e4m3)
   if constexpr (SCALED) {
     // e4m3: a slice is one k-step and one scale block.  Slices kt+1..kt+NS-2 stay in flight
     // while slice kt is multiplied straight out of its stage; the barrier at the top of each
@@ -222,7 +222,6 @@ __global__ __launch_bounds__(WN * WM * kWave) void stream_kernel(Args g) {
     }
     // An m-block holds its expert's rows first and padding after, so 16-row fragments from
     // ceil(valid / 16) on are all padding: their products are skipped (accumulators stay 0).
-    int fmv;
     {
       const int s_lo = g.sorted_slots[row0 + min(lane, BM - 1)];
       const int s_hi = g.sorted_slots[row0 + min(lane + kWave, BM - 1)];
@@ -322,8 +321,7 @@ __global__ __launch_bounds__(WN * WM * kWave) void stream_kernel(Args g) {
   const int orow = (lane >> 4) * 4;
   if constexpr (UP) {
     float a[FMW][FN][4];
-    #pragma unroll
-    for (int i = 0; i < FMW; ++i)
+    auto silu_mul = [&](int i) {
       #pragma unroll
       for (int j = 0; j < FN; ++j)
         #pragma unroll
@@ -331,12 +329,17 @@ __global__ __launch_bounds__(WN * WM * kWave) void stream_kernel(Args g) {
           const float gt = acc[i][j][v], up = acc[i][j + FN][v];
           a[i][j][v] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
         }
+    };
     if constexpr (OUT == OUT_E4M3) {
+      // Fragments from fmv on hold only padding rows, whose accumulators are exactly 0: their
+      // codes are 0 and their scales 1 (what amax = 0 gives), stored without the arithmetic.
       // amax of each row over the tile's 128 columns (one activation group), across waves
       __syncthreads();                                   // LDS is free: the ring is drained
       float* red = reinterpret_cast<float*>(lds);
       #pragma unroll
-      for (int i = 0; i < FMW; ++i)
+      for (int i = 0; i < FMW; ++i) {
+        if (fi(i) >= fmv) break;
+        silu_mul(i);
         #pragma unroll
         for (int v = 0; v < 4; ++v) {
           float m = 0.0f;
@@ -346,6 +349,7 @@ __global__ __launch_bounds__(WN * WM * kWave) void stream_kernel(Args g) {
           for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
           if (ocol == 0) red[wn * BM + fi(i) * 16 + orow + v] = m;
         }
+      }
       __syncthreads();
       uint8_t* act = reinterpret_cast<uint8_t*>(g.out);
       #pragma unroll
@@ -353,18 +357,35 @@ __global__ __launch_bounds__(WN * WM * kWave) void stream_kernel(Args g) {
         #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int m = fi(i) * 16 + orow + v;
-          float amax = 0.0f;
-          #pragma unroll
-          for (int w = 0; w < WN; ++w) amax = fmaxf(amax, red[w * BM + m]);
-          const float s = (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
           const size_t rowoff = (size_t)(row0 + m) * g.n_out + n0 + wn * WTN;
-          #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            act[rowoff + j * 16 + ocol] = (uint8_t)f32_to_e4m3(a[i][j][v] / s);
+          float s = 1.0f;
+          if (fi(i) < fmv) {
+            float amax = 0.0f;
+            #pragma unroll
+            for (int w = 0; w < WN; ++w) amax = fmaxf(amax, red[w * BM + m]);
+            s = (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
+            // quotient in fp32, then the gfx950 convert (round to nearest even, sign kept);
+            // the clamp keeps it within +-448, where the convert saturates nothing and
+            // matches f32_to_e4m3 on every value
+            #pragma unroll
+            for (int j = 0; j < FN; j += 2) {
+              const float q0 = fminf(fmaxf(a[i][j][v] / s, -kE4M3Max), kE4M3Max);
+              const float q1 =
+                  (j + 1 < FN) ? fminf(fmaxf(a[i][j + 1][v] / s, -kE4M3Max), kE4M3Max) : 0.0f;
+              const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+              act[rowoff + j * 16 + ocol] = (uint8_t)pk;
+              if (j + 1 < FN) act[rowoff + (j + 1) * 16 + ocol] = (uint8_t)(pk >> 8);
+            }
+          } else {
+            #pragma unroll
+            for (int j = 0; j < FN; ++j) act[rowoff + j * 16 + ocol] = 0;
+          }
           if (wn == 0 && ocol == 0)
             g.out_scales[(size_t)(row0 + m) * (g.n_out / kGroup) + n0 / kGroup] = s;
         }
     } else {
+      #pragma unroll
+      for (int i = 0; i < FMW; ++i) silu_mul(i);
       #pragma unroll
       for (int i = 0; i < FMW; ++i)
         #pragma unroll

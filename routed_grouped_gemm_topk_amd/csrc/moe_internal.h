@@ -130,24 +130,32 @@ __device__ __forceinline__ int xcd_logical(int b, int valid) {
 // G m-blocks sweep the n-blocks, n-block-major inside a group.  A group never holds two
 // experts, so concurrent workgroups of one XCD share their weight tiles (each fetched once)
 // and their gathered rows.  With one m-block per expert this is n-block order.
-// logical / n_blocks is an m-block of the expert that owns `logical`.
+// logical / n_blocks is an m-block of the expert that owns `logical`, so one read of the tile
+// table gives the expert; offsets are multiples of the m-block size and the tile table lists
+// m-blocks expert by expert, so m-block mt starts at row mt * BMT.
+struct TileRef {
+  int e, mt, nt, row0;   // expert, m-block, n-block, first row of the m-block
+};
 template <int BMT, int G>
-__device__ __forceinline__ void grouped_tile(int logical, int n_blocks, const int32_t* tiles,
-                                             const int32_t* offsets, int& mt, int& nt) {
-  const int e = tiles[2 * (logical / n_blocks)];
-  const int base = offsets[e] / BMT;
-  const int M = (offsets[e + 1] - offsets[e]) / BMT;
+__device__ __forceinline__ TileRef grouped_tile(int logical, int n_blocks, const int32_t* tiles,
+                                                const int32_t* offsets) {
+  TileRef t;
+  t.e = tiles[2 * (logical / n_blocks)];
+  const int base = offsets[t.e] / BMT;
+  const int M = (offsets[t.e + 1] - offsets[t.e]) / BMT;
   const int r = logical - base * n_blocks;          // 0 <= r < M * n_blocks
   const int full = M / G;
   if (r < full * G * n_blocks) {
     const int g = r / (G * n_blocks), w = r - g * G * n_blocks;
-    nt = w / G;
-    mt = base + g * G + (w - nt * G);
+    t.nt = w / G;
+    t.mt = base + g * G + (w - t.nt * G);
   } else {
     const int rem = M - full * G, w = r - full * G * n_blocks;
-    nt = w / rem;
-    mt = base + full * G + (w - nt * rem);
+    t.nt = w / rem;
+    t.mt = base + full * G + (w - t.nt * rem);
   }
+  t.row0 = t.mt * BMT;
+  return t;
 }
 
 // Block b -> logical tile, in chunks: the logical order is cut into chunks of C tiles that are
