@@ -199,9 +199,17 @@ __device__ void finish_layout(const int* cnt, int* tb, int* off, int* wsum, int 
     tiles[2 * i] = e;
     tiles[2 * i + 1] = r;
   }
-  // sentinel in padding rows (after each expert's slots) and the unused tail
-  for (int e = tid; e < E; e += kAlignThreads)
-    for (int r = off[e] + cnt[e]; r < off[e + 1]; ++r) sorted_slots[r] = N;
+  // sentinel in padding rows (after each expert's slots) and the unused tail.  An expert has
+  // fewer than BM padding rows: from 64-row blocks on, wave w takes experts w, w + 16, ...,
+  // its lanes writing an expert's padding rows 64 at a time (whole stores instead of one row
+  // per lane per store); below that each thread writes its expert's few rows.
+  if (BM >= kWave) {
+    for (int e = wave; e < E; e += kAlignWaves)
+      for (int r = off[e] + cnt[e] + lane; r < off[e + 1]; r += kWave) sorted_slots[r] = N;
+  } else {
+    for (int e = tid; e < E; e += kAlignThreads)
+      for (int r = off[e] + cnt[e]; r < off[e + 1]; ++r) sorted_slots[r] = N;
+  }
   for (int r = off[E] + tid; r < rows_max; r += kAlignThreads) sorted_slots[r] = N;
   __syncthreads();
 }

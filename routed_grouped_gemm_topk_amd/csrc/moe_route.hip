@@ -44,8 +44,11 @@ hipError_t launch_route(const Resolved& r, const float* logits, int renorm, int3
 }
 
 // Routing, then alignment of its ids: two launches on one stream, no host synchronisation.
-// (Routing needs a wavefront per token across the whole GPU; a one-workgroup fusion with the
-// alignment measured slower than the two launches: its shuffle and exp work is bound to one CU.)
+// Routing needs its waves spread over the GPU (a token's top-k is a chain of dependent
+// wavefront reductions, about 5 us per token), so a one-workgroup fusion with the alignment
+// is bound to one CU's latency; a fusion that keeps the routing spread has to hand the ids
+// across workgroups (a completion ticket with device-scope fences), and those fences, which
+// write back and invalidate the L2 of each of the 8 XCDs, cost more than the launch saved.
 hipError_t launch_route_align(const Resolved& r, const float* logits, int renorm, int32_t* topk_ids,
                               float* topk_w, int32_t* counts, int32_t* offsets,
                               int32_t* sorted_slots, int32_t* slot_row, int32_t* tiles,
