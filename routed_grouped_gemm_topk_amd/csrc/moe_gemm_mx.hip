@@ -22,9 +22,17 @@
 //     ring: per slice BM rows x 128 B of gathered codes, 2*BNA weight rows x 64 B, and the
 //     4 x 2*BNA scale bytes of the slice (scales are stored [E, H/32, 2I], so a slice's scales
 //     are 4 contiguous runs);
-//   * K need only be a multiple of 64: copies of chunks past K read a static zero area;
+//   * K need only be a multiple of 64: copies of chunks past K read a static zero area (only
+//     the last slice can hold such chunks; the copies of the slices before it advance a
+//     pointer per slice and check nothing);
 //   * tile order: expert by expert, groups of 4 m-blocks sweep the n-blocks; padding rows
-//     read zeros and their 16-row fragments are skipped; their act rows are not written.
+//     read zeros and their 16-row fragments are skipped; their act rows are not written;
+//   * epilogue in fp32 with the gfx950 units: exp through v_exp_f32 (__expf) and the
+//     reciprocal v_rcp_f32 for the SwiGLU's division, a multiply by 1/out_scale, and the
+//     e4m3 convert (v_cvt_pk_fp8_f32, round to nearest even) after a clamp to +-448.  Each of
+//     these is within a few ulp of the correctly rounded fp32 operation, so a code can move
+//     by one step only for a value within that distance of a rounding midpoint, which the
+//     fp32 accumulation order already does against the oracle.
 #include "moe_internal.h"
 
 namespace moe {
@@ -39,9 +47,11 @@ __device__ __attribute__((aligned(16))) char g_zero[256];
 
 // 16-byte chunk swizzle of rows of RB bytes: chunk c of row r sits at c ^ swz<RB>(r), which
 // puts the fragment reads (16 consecutive rows at one chunk) in 16 distinct 4-bank groups.
+// For 64-byte rows ((r >> 1) ^ (r >> 2)) & 3 also keeps every 8 consecutive rows in 8 distinct
+// groups of a 32-bank view ((r >> 2) & 3 alone does not; measured 1-5% faster).
 template <int RB>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (RB == 64) return (r >> 2) & 3;
+  if constexpr (RB == 64) return ((r >> 1) ^ (r >> 2)) & 3;
   else if constexpr (RB == 128) return (r & 7) ^ ((r >> 3) & 1);
   else return r & 15;
 }
@@ -94,7 +104,7 @@ __global__ __launch_bounds__(WN * WM * kWave) void mx_up_kernel(Args g) {
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wn = wave % WN;
   const int wm = wave / WN;
 
@@ -147,23 +157,54 @@ __global__ __launch_bounds__(WN * WM * kWave) void mx_up_kernel(Args g) {
     ssrc[i] = reinterpret_cast<const char*>(g.w_scales) +
               ((size_t)e * KB + skb[i]) * I2 + 2 * n0 + (b % WROWS);
   }
+  // Slices before KT_full hold no chunk at or past K: their copies read live rows (padding
+  // rows read the zero area with no step) from a pointer advanced by one step per slice; the
+  // last slice of a K that is not a whole number of slices checks each chunk.
+  const int KT_full = K / KS;
+  const char* cur[NQW];
+  int cstep[NQW];
+  uint32_t cdst[NQW];
+  #pragma unroll
+  for (int i = 0; i < NQW; ++i) {
+    const int q = min(wave * NQW + i, NQ - 1);
+    cur[i] = live[i] ? src[i] : reinterpret_cast<const char*>(g_zero);
+    cstep[i] = live[i] ? step[i] : 0;
+    cdst[i] = q < NQ_X ? q * 1024 : W_OFF + (q - NQ_X) * 1024;
+  }
+  const char* scur[NSW];
+  #pragma unroll
+  for (int i = 0; i < NSW; ++i) scur[i] = ssrc[i];
   const uint32_t lds_base = lds_u32(lds);
+  // copies of slice kt (called with kt = 0, 1, 2, ... in order, then KT for past the end)
   auto issue = [&](int buf, int kt) {
-    const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + buf * STAGE);
-    const int k0 = kt * KS;
-    #pragma unroll
-    for (int i = 0; i < NQW; ++i) {
-      const int q = min(wave * NQW + i, NQ - 1);
-      const uint32_t dst = q < NQ_X ? st + q * 1024 : st + W_OFF + (q - NQ_X) * 1024;
-      const bool ok = live[i] && k0 + kof[i] < K;
-      lds_dma16(ok ? src[i] + (size_t)kt * step[i] : g_zero, __builtin_amdgcn_readfirstlane(dst));
-    }
-    #pragma unroll
-    for (int i = 0; i < NSW; ++i) {
-      const int q = min(wave * NSW + i, NS_REAL - 1);
-      const bool ok = SB * kt + skb[i] < KB;
-      lds_dma4(ok ? ssrc[i] + (size_t)kt * SB * I2 : g_zero,
-               __builtin_amdgcn_readfirstlane(st + S_OFF + q * 256));
+    const uint32_t st = lds_base + buf * STAGE;
+    if (kt < KT_full) {
+      #pragma unroll
+      for (int i = 0; i < NQW; ++i) {
+        lds_dma16(cur[i], __builtin_amdgcn_readfirstlane(st + cdst[i]));
+        cur[i] += cstep[i];
+      }
+      #pragma unroll
+      for (int i = 0; i < NSW; ++i) {
+        const int q = min(wave * NSW + i, NS_REAL - 1);
+        lds_dma4(scur[i], __builtin_amdgcn_readfirstlane(st + S_OFF + q * 256));
+        scur[i] += (size_t)SB * I2;
+      }
+    } else {
+      const int k0 = kt * KS;
+      #pragma unroll
+      for (int i = 0; i < NQW; ++i) {
+        const bool ok = live[i] && k0 + kof[i] < K;
+        lds_dma16(ok ? src[i] + (size_t)kt * step[i] : reinterpret_cast<const char*>(g_zero),
+                  __builtin_amdgcn_readfirstlane(st + cdst[i]));
+      }
+      #pragma unroll
+      for (int i = 0; i < NSW; ++i) {
+        const int q = min(wave * NSW + i, NS_REAL - 1);
+        const bool ok = SB * kt + skb[i] < KB;
+        lds_dma4(ok ? ssrc[i] + (size_t)kt * SB * I2 : reinterpret_cast<const char*>(g_zero),
+                 __builtin_amdgcn_readfirstlane(st + S_OFF + q * 256));
+      }
     }
   };
 
@@ -205,12 +246,13 @@ __global__ __launch_bounds__(WN * WM * kWave) void mx_up_kernel(Args g) {
   // Slices kt+1..kt+NS-2 in flight; the barrier at the top of slice kt publishes it and
   // retires the stage of slice kt-1, which is refilled at once.
   #pragma unroll
-  for (int s = 0; s < NS - 1; ++s) issue(s, min(s, KT - 1));
+  for (int s = 0; s < NS - 1; ++s) issue(s, s < KT ? s : KT);
   int buf = 0;
   for (int kt = 0; kt < KT; ++kt) {
     wait_vmcnt<(NS - 2) * OPS>();
     __syncthreads();
-    issue(buf == 0 ? NS - 1 : buf - 1, min(kt + NS - 1, KT - 1));   // past the end: repeat, unread
+    // past the end: a slice of zero chunks (the checked path), never read
+    issue(buf == 0 ? NS - 1 : buf - 1, kt + NS - 1 < KT ? kt + NS - 1 : KT);
     const char* stg = lds + buf * STAGE;
     #pragma unroll
     for (int kk = 0; kk < KSL; ++kk) {
@@ -241,7 +283,10 @@ __global__ __launch_bounds__(WN * WM * kWave) void mx_up_kernel(Args g) {
   // ---- epilogue: lane holds weight rows 4*fq + v (v = 0..3) of fragment f for token fr:
   // (gate, linear) of act column c and of column c + 1 -----------------------------------------
   const float xs = *g.x_scale;
-  const float ys = *g.out_scale;
+  const float inv_ys = 1.0f / *g.out_scale;
+  bool row_ok[FMW];
+  #pragma unroll
+  for (int i = 0; i < FMW; ++i) row_ok[i] = g.sorted_slots[row0 + min(fi(i) * 16 + fr, BM - 1)] < g.n_slots;
   #pragma unroll
   for (int f = 0; f < FW; ++f) {
     const int wr = 2 * n0 + wn * WTW + f * 16 + 4 * fq;   // first of this lane's 4 weight rows
@@ -251,19 +296,21 @@ __global__ __launch_bounds__(WN * WM * kWave) void mx_up_kernel(Args g) {
     for (int i = 0; i < FMW; ++i) {
       if (fi(i) >= fmv) break;
       const int m = fi(i) * 16 + fr;
-      if (g.sorted_slots[row0 + m] >= g.n_slots) continue;
-      uint32_t code[2];
+      if (!row_ok[i]) continue;
+      float q[2];
       #pragma unroll
       for (int p = 0; p < 2; ++p) {
         const float h_g = fmaf(acc[f][i][2 * p], xs, b[2 * p]);
         const float h_l = fmaf(acc[f][i][2 * p + 1], xs, b[2 * p + 1]);
         const float gt = fminf(h_g, g.limit);
         const float ln = fminf(fmaxf(h_l, -g.limit), g.limit);
-        const float a = gt / (1.0f + expf(-g.alpha * gt));
-        code[p] = f32_to_e4m3(fmaf(a, ln, a) / ys);
+        const float a = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-g.alpha * gt));
+        // act / out_scale, clamped to +-448 (the convert then saturates nothing), converted
+        // with round to nearest even
+        q[p] = fminf(fmaxf(fmaf(a, ln, a) * inv_ys, -kE4M3Max), kE4M3Max);
       }
-      *reinterpret_cast<uint16_t*>(g.act + (size_t)(row0 + m) * g.I + c) =
-          (uint16_t)(code[0] | (code[1] << 8));
+      const uint32_t codes = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+      *reinterpret_cast<uint16_t*>(g.act + (size_t)(row0 + m) * g.I + c) = (uint16_t)codes;
     }
   }
 }
