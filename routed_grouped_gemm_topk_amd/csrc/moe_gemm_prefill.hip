@@ -17,7 +17,9 @@
 //   * k-slices of BK = 64 (128 bytes per row) in a ring of NS LDS stages without padding:
 //     the 16-byte chunk c of row r sits at position c ^ ((r & 7) ^ ((r >> 3) & 1)),
 //     conflict-free for the fragment reads (32 consecutive rows at one k offset);
-//   * global -> LDS copies by direct-to-LDS DMA (below), NS-1 slices in flight;
+//   * global -> LDS copies by direct-to-LDS DMA (below), NS-1 slices in flight; the 256-row
+//     tiles give the m-block rows a ring of two stages and the weight rows one of three, and
+//     spread each slice's copies over the k-steps of the next slice;
 //   * fragment reads of the next 16-wide k step overlap the MFMAs of the current one, one
 //     read after each MFMA;
 //   * with a workspace, the tiles of the last, partly filled round of workgroups are cut
@@ -127,7 +129,8 @@ __device__ __forceinline__ void buf_dma16(i32x4 rsrc, uint32_t voff, uint32_t so
 // and padding rows of the gathered operand at an offset past the end of X, read as zeros
 // without a memory access.  Measured against the global_load_lds form on the Mixtral-shaped
 // workload: 2% faster, bit-identical.
-template <int BMT, int BK, int NS, int BNA, bool UP, int WM, int WN, bool BUF = false>
+// WS: stages of a separate weight ring (0: rows and weights share the NS-stage ring)
+template <int BMT, int BK, int NS, int BNA, bool UP, int WM, int WN, bool BUF = false, int WS = 0>
 __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
   constexpr int ROWB = BK * 2, KK = BK / 16, NW = WN * WM;
   constexpr int BROWS = UP ? 2 * BNA : BNA;
@@ -142,8 +145,14 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
   constexpr int CPR = ROWB / 16;
   static_assert(NQ % NW == 0, "copies split evenly over the waves");
   static_assert(NS >= 2 && (NS - 1) * NQW <= 63, "vmcnt range");
+  // SPLIT (WS > NS): the m-block rows and the weight rows have rings of their own, of NS = 2
+  // and WS = 3 stages, and each wave copies only rows or only weights (BUF); see the k-loop.
+  constexpr bool SPLIT = WS > NS;
+  constexpr int ASTAGE = BMT * ROWB, WSTAGE = BROWS * ROWB;
+  static_assert(!SPLIT || (BUF && NS == 2 && WS == 3 && KK == 4 && NQW == 8), "split rings");
+  constexpr int LDS_BYTES = SPLIT ? NS * ASTAGE + WS * WSTAGE : NS * STAGE;
 
-  __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -192,18 +201,38 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
   }
   const char* src[BUF ? 1 : NQW];
   uint32_t voff[BUF ? NQW : 1];
+  // Slots of the m-block (to count its rows that hold slots) and of the rows this wave
+  // gathers, all loaded before any is used: one memory round trip per tile (a slot loaded
+  // where it is used made the compiler wait for each in turn: one round trip per copy).
+  int mslot[BMT / kWave];
+  #pragma unroll
+  for (int r0 = 0; r0 < BMT; r0 += kWave) mslot[r0 / kWave] = g.sorted_slots[row0 + r0 + lane];
+  int slot[UP ? NQW : 1];
+  if constexpr (UP) {
+    #pragma unroll
+    for (int i = 0; i < NQW; ++i)
+      if ((wave * NQW + i) * ROWS_PER_Q < BMT)    // wave-uniform: copy i gathers rows
+        slot[i] = g.sorted_slots[row0 + (wave * NQW + i) * ROWS_PER_Q + lane / CPR];
+  }
+  // Rows of the m-block that hold slots come first, padding after: this wave's 32-row
+  // fragments from fmv on are all padding, and their reads and MFMAs are skipped.
+  int valid = 0;
+  #pragma unroll
+  for (int r0 = 0; r0 < BMT; r0 += kWave) valid += __popcll(__ballot(mslot[r0 / kWave] < g.n_slots));
+  const int fmv = __builtin_amdgcn_readfirstlane(min(FM, max(0, (valid - mrow0 + 31) / 32)));
   #pragma unroll
   for (int i = 0; i < NQW; ++i) {
     const int q = wave * NQW + i;
     const int r = q * ROWS_PER_Q + lane / CPR;      // row of the stage this lane fills
     const int cc = (lane % CPR) ^ swz<ROWB>(r);      // chunk that belongs at this position
-    if (r < BMT) {
+    if (q * ROWS_PER_Q < BMT) {
       if (UP) {
-        const int s = g.sorted_slots[row0 + r];
+        const int s = slot[i];
+        const int t = s / g.top_k;                   // sentinel slots too: no branch
         if constexpr (BUF)
-          voff[i] = (s < g.n_slots) ? (uint32_t)((s / g.top_k) * K * 2 + cc * 16) : 0x80000000u;
+          voff[i] = (s < g.n_slots) ? (uint32_t)(t * K * 2 + cc * 16) : 0x80000000u;
         else
-          src[i] = (s < g.n_slots) ? g.a_src + (size_t)(s / g.top_k) * K * 2 + cc * 16
+          src[i] = (s < g.n_slots) ? g.a_src + (size_t)t * K * 2 + cc * 16
                                    : g_zero_row + cc * 16;
       } else {
         if constexpr (BUF) voff[i] = (uint32_t)(r * K * 2 + cc * 16);
@@ -220,13 +249,45 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
     }
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
-  auto issue = [&](int buf, int kt) {
-    const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + buf * STAGE + wave * NQW * 1024);
+  // copies [I0, I0 + N) of this wave for slice kt into stage buf of the wave's ring
+  auto issue_part = [&](auto i0_tag, auto n_tag, int buf, int kt) {
+    constexpr int I0 = decltype(i0_tag)::value, N = decltype(n_tag)::value;
+    uint32_t st;
+    if constexpr (SPLIT)
+      st = a_wave ? lds_base + buf * ASTAGE + wave * NQW * 1024
+                  : lds_base + NS * ASTAGE + buf * WSTAGE + wave * NQW * 1024 - ASTAGE;
+    else
+      st = lds_base + buf * STAGE + wave * NQW * 1024;
+    st = __builtin_amdgcn_readfirstlane(st);
     const int koff = kt * ROWB;
     #pragma unroll
-    for (int i = 0; i < NQW; ++i) {
+    for (int i = I0; i < I0 + N; ++i) {
       if constexpr (BUF) buf_dma16(rsrc, voff[i], (uint32_t)koff, st + i * 1024);
       else lds_dma16(src[i] + koff, st + i * 1024);
+    }
+  };
+  auto issue = [&](int buf, int kt) {
+    issue_part(std::integral_constant<int, 0>{}, std::integral_constant<int, NQW>{}, buf, kt);
+  };
+  // SPLIT: a slice's copies go out in parts, part p before k-step p-1 of the next slice (part
+  // 0 right after the barrier): rows in parts of 3, 3, 2 (p = 0..2), weights of 2 (p = 0..3).
+  auto issue_p = [&](int p, int buf, int kt) {
+    if constexpr (SPLIT) {
+      using C0 = std::integral_constant<int, 0>;
+      using C2 = std::integral_constant<int, 2>;
+      using C3 = std::integral_constant<int, 3>;
+      using C4 = std::integral_constant<int, 4>;
+      using C6 = std::integral_constant<int, 6>;
+      if (a_wave) {
+        if (p == 0)      issue_part(C0{}, C3{}, buf, kt);
+        else if (p == 1) issue_part(C3{}, C3{}, buf, kt);
+        else if (p == 2) issue_part(C6{}, C2{}, buf, kt);
+      } else {
+        if (p == 0)      issue_part(C0{}, C2{}, buf, kt);
+        else if (p == 1) issue_part(C2{}, C2{}, buf, kt);
+        else if (p == 2) issue_part(C4{}, C2{}, buf, kt);
+        else             issue_part(C6{}, C2{}, buf, kt);
+      }
     }
   };
 
@@ -253,31 +314,23 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
       #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // Rows of the m-block that hold slots come first, padding after: this wave's 32-row
-  // fragments from fmv on are all padding, and their reads and MFMAs are skipped.
-  int fmv;
-  {
-    int valid = 0;
-    #pragma unroll
-    for (int r0 = 0; r0 < BMT; r0 += kWave)
-      valid += __popcll(__ballot(g.sorted_slots[row0 + r0 + lane] < g.n_slots));
-    fmv = __builtin_amdgcn_readfirstlane(min(FM, max(0, (valid - mrow0 + 31) / 32)));
-  }
 
   // Two fragment sets: one being multiplied, one being read.
   bf16x8 a0[FM], b0[NF], a1[FM], b1[NF];
   // PARTIAL: some of this wave's fragments are padding (checked per fragment, no schedule hint)
   auto main_loop = [&](auto partial_tag) {
     constexpr bool PARTIAL = decltype(partial_tag)::value;
-    auto read_frags = [&](bf16x8* af, bf16x8* bfr, int buf, int kk) {
-      const char* st = lds + buf * STAGE;
+    // buf: stage of the m-block rows; wbuf: stage of the weight rows (the same unless SPLIT)
+    auto read_frags = [&](bf16x8* af, bf16x8* bfr, int buf, int wbuf, int kk) {
+      const char* st = lds + (SPLIT ? buf * ASTAGE : buf * STAGE);
+      const char* sw = SPLIT ? lds + NS * ASTAGE + wbuf * WSTAGE - ASTAGE : st;
       #pragma unroll
       for (int i = 0; i < FM; ++i)
         if (!PARTIAL || i < fmv)
           af[i] = *reinterpret_cast<const bf16x8*>(st + (mrow0 + i * 32) * ROWB + lane_off[kk]);
       if (PARTIAL && fmv == 0) return;
       #pragma unroll
-      for (int j = 0; j < NF; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(st + b_row[j] + lane_off[kk]);
+      for (int j = 0; j < NF; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(sw + b_row[j] + lane_off[kk]);
     };
     auto mfmas = [&](const bf16x8* af, const bf16x8* bfr) {
       #pragma unroll
@@ -306,36 +359,71 @@ __global__ __launch_bounds__(WN * WM * kWave) void gemm_dma_kernel(Args g) {
     };
     // k-step kk of the slice in `buf`: multiply set (kk & 1) while reading the next k-step
     // (of this slice, or k-step 0 of the slice in `nbuf`) into the other set.
-    auto step = [&](int kk, int buf, int nbuf) {
+    auto step = [&](int kk, int buf, int nbuf, int wbuf, int nwbuf) {
       const int nb = (kk + 1 < KK) ? buf : nbuf;
+      const int nw = (kk + 1 < KK) ? wbuf : nwbuf;
       const int nk = (kk + 1 < KK) ? kk + 1 : 0;
-      if (kk & 1) { read_frags(a0, b0, nb, nk); mfmas(a1, b1); }
-      else        { read_frags(a1, b1, nb, nk); mfmas(a0, b0); }
+      if (kk & 1) { read_frags(a0, b0, nb, nw, nk); mfmas(a1, b1); }
+      else        { read_frags(a1, b1, nb, nw, nk); mfmas(a0, b0); }
       interleave();
     };
 
     // Ring of NS stages.  After the fragments of a slice's last k-step are read, one barrier
     // (a) publishes slice kt+1 (every wave waited for its own copies of it) and (b) frees the
-    // stage of slice kt, which is refilled at once with slice kt+NS; the last k-step's MFMAs
-    // then overlap the reads of slice kt+1's first fragments.  NS-1 slices stay in flight.
-    #pragma unroll
-    for (int s = 0; s < NS; ++s) issue(s, kbeg + min(s, KT - 1));
-    wait_vmcnt<(NS - 1) * NQW>();
+    // stage of slice kt, which is refilled with slice kt+NS; the last k-step's MFMAs then
+    // overlap the reads of slice kt+1's first fragments.  NS-1 slices stay in flight.
+    //
+    // SPLIT: the freed rows stage takes rows slice kt+2 and the freed weight stage weight
+    // slice kt+3, both in parts spread over the next k-steps (issue_p), so rows slice kt+2
+    // is complete before barrier kt+1 and weight slices kt+2 and kt+3 may be in flight
+    // there.  Measured against the single ring whose 64 copies all went out right after the
+    // barrier (timers in the loop: the waves whose copies were accepted last reached the next
+    // barrier last, the others waited there 35-42% of the time): down GEMM 4-6% faster, up
+    // GEMM unchanged, bit-identical.  Copying rows and weights in every wave, or only in the
+    // four waves that the issue arbiter favours, or the weights alone spread, was slower.
+    if constexpr (SPLIT) {
+      // rows: slice 0 and part 0 of slice 1; weights: slices 0, 1 and part 0 of slice 2
+      const int last = a_wave ? NS - 1 : WS - 1;
+      #pragma unroll
+      for (int s = 0; s < WS - 1; ++s)
+        if (s < last) issue(s, kbeg + min(s, KT - 1));
+      issue_p(0, last, kbeg + min(last, KT - 1));
+      if (a_wave) wait_vmcnt<3>();                 // rows slice 0 landed
+      else        wait_vmcnt<NQW + 2>();           // weight slice 0 landed
+    } else {
+      #pragma unroll
+      for (int s = 0; s < NS; ++s) issue(s, kbeg + min(s, KT - 1));
+      wait_vmcnt<(NS - 1) * NQW>();
+    }
     __syncthreads();
-    read_frags(a0, b0, 0, 0);
-    int buf = 0;
+    read_frags(a0, b0, 0, 0, 0);
+    // stage and slice whose parts are being issued (SPLIT)
+    int buf = 0, wbuf = 0, qbuf = a_wave ? NS - 1 : WS - 1, qslice = qbuf;
     for (int kt = 0; kt < KT; ++kt) {
       const int nbuf = (buf + 1 == NS) ? 0 : buf + 1;
+      const int nwbuf = SPLIT ? ((wbuf + 1 == WS) ? 0 : wbuf + 1) : nbuf;
       #pragma unroll
-      for (int kk = 0; kk < KK - 1; ++kk) step(kk, buf, nbuf);
+      for (int kk = 0; kk < KK - 1; ++kk) {
+        if constexpr (SPLIT) issue_p(kk + 1, qbuf, kbeg + min(qslice, KT - 1));
+        step(kk, buf, nbuf, SPLIT ? wbuf : buf, nwbuf);
+      }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // all reads of stage buf done
-      wait_vmcnt<(NS - 2) * NQW>();                          // this wave's slice kt+1 landed
+      // this wave's copies of slice kt+1 landed (SPLIT weights: slice kt+2 may be in flight)
+      if (SPLIT && !a_wave) wait_vmcnt<NQW>();
+      else                  wait_vmcnt<(NS - 2) * NQW>();
       __syncthreads();
       // past the last slice repeat slice KT-1 (in bounds, never read) so every iteration
       // leaves the same number of copies outstanding
-      issue(buf, kbeg + min(kt + NS, KT - 1));
-      step(KK - 1, buf, nbuf);              // after the last slice the reads are stale, unused
+      if constexpr (SPLIT) {
+        qbuf = a_wave ? buf : wbuf;
+        qslice = kt + (a_wave ? NS : WS);
+        issue_p(0, qbuf, kbeg + min(qslice, KT - 1));
+      } else {
+        issue(buf, kbeg + min(kt + NS, KT - 1));
+      }
+      step(KK - 1, buf, nbuf, SPLIT ? wbuf : buf, nwbuf);   // after the last slice: stale, unused
       buf = nbuf;
+      wbuf = nwbuf;
     }
     wait_vmcnt<0>();
   };
@@ -481,7 +569,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(Args g) {
   }
 }
 
-template <int BK, int NS, int BNA, bool UP, int WM = 1, int BMT = BM, int WN = 4, bool BUF = false>
+template <int BK, int NS, int BNA, bool UP, int WM = 1, int BMT = BM, int WN = 4, bool BUF = false, int WS = 0>
 hipError_t run_dma(Args a, hipStream_t s) {
   // sized by the host-side tile bound; blocks past the device-side tile count exit at once
   const int64_t grid = xcd_chunked_grid<kChunk>((int64_t)a.tiles_max * ((a.n_out + BNA - 1) / BNA));
@@ -490,7 +578,7 @@ hipError_t run_dma(Args a, hipStream_t s) {
   if (!split) a.slots = 0;
   static_assert(BK == kSplitBK, "the K-split tail assumes 64-wide k-slices");
   a.grid_tiles = (int)grid;
-  hipLaunchKernelGGL((gemm_dma_kernel<BMT, BK, NS, BNA, UP, WM, WN, BUF>),
+  hipLaunchKernelGGL((gemm_dma_kernel<BMT, BK, NS, BNA, UP, WM, WN, BUF, WS>),
                      dim3((unsigned)(grid + (split ? a.slots : 0))), dim3(WN * WM * kWave), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
@@ -542,7 +630,7 @@ hipError_t launch_up_prefill(const Resolved& r, const void* x, const void* w13,
   // MUBUF copies need X's byte size below 2^31 (32-bit offsets; padding at 2^31 reads zeros)
   if (r.BM == 256) {
     if ((int64_t)r.T * r.H * 2 < ((int64_t)1 << 31))
-      return pf::run_dma<64, 2, 128, true, 4, 256, 2, true>(a, s);
+      return pf::run_dma<64, 2, 128, true, 4, 256, 2, true, 3>(a, s);
     return pf::run_dma<64, 2, 128, true, 4, 256, 2>(a, s);
   }
   if (r.I % 256 == 0) return pf::run_dma<64, 2, 256, true, 2>(a, s);
@@ -573,7 +661,7 @@ hipError_t launch_down_prefill(const Resolved& r, const void* act, const void* w
   a.w_expert_elems = (int64_t)r.H * r.I;
   // H a multiple of 64 but not of 128: the last 128-wide n-block is half used
   if (r.BM == 256) {
-    if (r.H % 256 == 0) return pf::run_dma<64, 2, 256, false, 4, 256, 2, true>(a, s);
+    if (r.H % 256 == 0) return pf::run_dma<64, 2, 256, false, 4, 256, 2, true, 3>(a, s);
     return pf::run_dma<64, 2, 128, false, 4, 256, 2>(a, s);
   }
   if (r.H % 256 == 0) return pf::run_dma<64, 3, 256, false, 2>(a, s);
