@@ -197,7 +197,10 @@ def warm_up(step, n, min_seconds=0.1):
 
 
 SWEEP_KEY_NOTE = ("  bm: the shard's block size, keyed on its local slots per active local "
-                  "expert; page-key bm: the same rule keyed on T*k/E_total.")
+                  "expert; page-key bm: the same rule keyed on T*k/E_total.  The best, bm "
+                  "(same runs) and page-key times all come from one timed run per candidate "
+                  "block size, so they compare like for like; the bm columns to the left are "
+                  "bm's own run.")
 
 
 def shard_block_m(moe, n_loc, active, x_dtype, w_dtype):
@@ -313,6 +316,10 @@ def sweep(args):
             pt["best_layer_ms"] = round(best[1]["layer"], 5)
             pt["best_up_ms"] = round(best[1]["up"], 5)
             pt["layer_ms_by_block_m"] = by_bm
+            # the shard's and the page's block sizes compared with the best from the same
+            # candidate runs (like for like; layer_ms is the shard key's own run)
+            if bm0 in by_bm:
+                pt["shard_key_layer_ms"] = by_bm[bm0]
             if bm_page in by_bm:
                 pt["page_key_layer_ms"] = by_bm[bm_page]
         print(json.dumps(pt), flush=True)
@@ -327,6 +334,7 @@ def sweep(args):
                 ("layer TF/s", "layer_TFLOP/s")]
         if cands:
             cols += [("best bm", "best_block_m"), ("best layer ms", "best_layer_ms"),
+                     ("bm layer ms (same runs)", "shard_key_layer_ms"),
                      ("page-key bm", "page_key_block_m"), ("page-key layer ms", "page_key_layer_ms")]
         write_sweep_table(args, base, torch.cuda.get_device_name(dev), cols, rows_md,
                           note=SWEEP_KEY_NOTE)
@@ -405,6 +413,8 @@ def sweep_mx(args, base):
         if by_bm:
             best = min(by_bm, key=by_bm.get)
             pt.update(best_block_m=best, best_up_ms=by_bm[best], up_ms_by_block_m=by_bm)
+            if bm0 in by_bm:
+                pt["shard_key_up_ms"] = by_bm[bm0]
             if bm_page in by_bm:
                 pt["page_key_up_ms"] = by_bm[bm_page]
         print(json.dumps(pt), flush=True)
@@ -417,6 +427,7 @@ def sweep_mx(args, base):
                 ("roofline frac", "up_roofline_frac")]
         if cands:
             cols += [("best bm", "best_block_m"), ("best ms", "best_up_ms"),
+                     ("bm ms (same runs)", "shard_key_up_ms"),
                      ("page-key bm", "page_key_block_m"), ("page-key ms", "page_key_up_ms")]
         write_sweep_table(args, base, torch.cuda.get_device_name(dev), cols, rows_md,
                           note=f"  Peak: {peak_tf} TFLOP/s (fp8 MFMA), {PEAK_HBM_GBS / 1000} TB/s."
