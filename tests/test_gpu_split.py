@@ -6,7 +6,9 @@ ascending part order before the epilogue. Each case below is sized so that both 
 split (checked from the oracle's tile count), and the outputs are compared with the oracle
 (layer tolerance 2e-2), with the same calls made without workspace (no split: they differ only
 by the fp32 summation order, then one bf16 rounding), with a second run (bit-identical) and
-with moe_forward (bit-identical).
+with moe_forward (bit-identical).  Which tiles split, and into how many parts, depends on the
+device's compute-unit count; the workspace shows the units the kernels wrote, which must be the
+ones predicted from that count.
 """
 import sys
 
@@ -88,10 +90,31 @@ def test_gemm_split_parity(device, label):
                                   a["offsets"], a["tiles"], a["num_tiles"], so, workspace)
         return so
 
+    def units_written(n_units, pw):
+        # K-split unit u writes its fp32 partial tile at u * (block_m x pw) floats of the
+        # workspace; its first row always holds a slot.  The workspace was filled with 0xFF
+        # (NaN), so written units start with a finite value and the next one with NaN.
+        f = ws.view(torch.float32)
+        stride = bm * pw
+        first = [float(f[u * stride].item()) for u in range(min(n_units + 1, f.numel() // stride))]
+        return first
+
     act1 = up_gemm(ws)
+    torch.cuda.synchronize()
+    # the split the kernels chose follows the device's compute-unit count (predicted above)
+    first = units_written(up[0] * up[1], 2 * bna_up)
+    assert all(np.isfinite(first[: up[0] * up[1]])), "a predicted up K-split unit was not written"
+    if len(first) > up[0] * up[1]:
+        assert np.isnan(first[up[0] * up[1]]), "more up K-split units than predicted"
     act2 = up_gemm(ws)
     act_plain = up_gemm(None)
+    ws.fill_(0xFF)
     so1 = down_gemm(act1, ws)
+    torch.cuda.synchronize()
+    first = units_written(down[0] * down[1], bna_down)
+    assert all(np.isfinite(first[: down[0] * down[1]])), "a predicted down K-split unit was not written"
+    if len(first) > down[0] * down[1]:
+        assert np.isnan(first[down[0] * down[1]]), "more down K-split units than predicted"
     so2 = down_gemm(act1, ws)
     so_plain = down_gemm(act1, None)
     out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=device)
