@@ -203,6 +203,79 @@ SWEEP_KEY_NOTE = ("  bm: the shard's block size, keyed on its local slots per ac
                   "bm's own run.")
 
 
+def routing_compare(moe, cfg, dev, calls=100, per_graph=20):
+    """moe_route_align against moe_route then moe_align on the same logits, in microseconds per
+    call: back-to-back eager calls (what a caller pays per call, launch overhead included) and
+    the same calls replayed from a HIP graph (launch overhead removed).  The two kinds are
+    measured alternately, three times each; the best of each is kept."""
+    import numpy as np
+    import torch
+    from moe_inputs import make_logits
+    p = moe.make_problem(cfg.T, cfg.H, cfg.I, cfg.E, cfg.top_k, cfg.x_dtype, cfg.w_dtype)
+    lg = torch.from_numpy(make_logits(cfg, 0).astype(np.float32)).to(dev)
+    a = moe.alloc_align(p, dev)
+    ids = torch.empty((cfg.T, cfg.top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((cfg.T, cfg.top_k), dtype=torch.float32, device=dev)
+    outs = (a["counts"], a["offsets"], a["sorted_slots"], a["slot_row"], a["tiles"],
+            a["num_tiles"], a["n_invalid"])
+
+    def one():
+        moe.moe_route_align(p, lg, cfg.renormalize, ids, w, *outs)
+
+    def two():
+        moe.moe_route(p, lg, cfg.renormalize, ids, w)
+        moe.moe_align(p, ids, *outs)
+
+    def events():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def eager(fn):
+        for _ in range(10):
+            fn()
+        e0, e1 = events()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(calls):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / calls
+
+    def graph(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                fn()
+        for _ in range(3):
+            g.replay()
+        e0, e1 = events()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(calls // per_graph):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (calls // per_graph * per_graph)
+
+    t = {"one_eager": [], "two_eager": [], "one_graph": [], "two_graph": []}
+    for _ in range(3):
+        t["one_eager"].append(eager(one))
+        t["two_eager"].append(eager(two))
+        t["one_graph"].append(graph(one))
+        t["two_graph"].append(graph(two))
+    best = {k: min(v) for k, v in t.items()}
+    return {"slots": cfg.T * cfg.top_k,
+            "route_align_us": round(best["one_eager"], 2),
+            "route_then_align_us": round(best["two_eager"], 2),
+            "route_align_us_graph": round(best["one_graph"], 2),
+            "route_then_align_us_graph": round(best["two_graph"], 2)}
+
+
 def shard_block_m(moe, n_loc, active, x_dtype, w_dtype):
     """Block size of one expert-parallel shard, keyed on its own dispatch counts: the slots it
     received per local expert that received any (an expert-parallel dispatch exchanges the
@@ -509,6 +582,9 @@ def main():
                               "layer_gbps_algorithmic", "kernels", "roofline")}
         res[EXTRA_KEY.get(name, name)]["pct_hbm_peak_layer"] = round(
             100 * r["layer_gbps_algorithmic"] / PEAK_HBM_GBS, 2)
+        # the router producer on this workload's logits: one call against route, then align
+        import routed_grouped_gemm_topk_amd as moe
+        res[EXTRA_KEY.get(name, name)]["routing"] = routing_compare(moe, CONFIGS[name], dev)
     print(json.dumps(res), flush=True)
 
 
@@ -630,22 +706,9 @@ def run_workload(cfg, args, dev, cpu_on, block_m=0, routing=None):
 
     routing_cmp = None
     if routing:
-        # the same work as two launches (moe_route, then moe_align), for comparison
-        def two_launches():
-            moe.moe_route(p, logits, cfg.renormalize, r_ids, r_w)
-            moe.moe_align(p, r_ids, a["counts"], a["offsets"], a["sorted_slots"], a["slot_row"],
-                          a["tiles"], a["num_tiles"], a["n_invalid"])
-        for _ in range(3):
-            two_launches()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(args.steps):
-            two_launches()
-        e1.record()
-        torch.cuda.synchronize()
+        # the step's route_align stage, and the call against route then align on its own
         routing_cmp = {"route_align_ms": round(kern_ms["route_align"], 5),
-                       "route_then_align_ms": round(e0.elapsed_time(e1) / args.steps, 5)}
+                       **routing_compare(moe, cfg, dev)}
 
     work, active = algorithmic_work(cfg, case.ids_host, bm, rows, mt)
     if routing:

@@ -176,10 +176,17 @@ int moe_route(const moe_problem* p, const float* logits, int renormalize, int32_
               float* topk_weights, void* stream);
 
 /*
- * moe_route_align -- moe_route followed by moe_align on its ids, as one call: the routing
- * launch (a wavefront per token) and the alignment launches on `stream`, with no host
- * synchronisation between them.  Arguments and outputs are those of the two calls; results are
- * identical to calling them in sequence.
+ * moe_route_align -- moe_route followed by moe_align on its ids, as one call.
+ * ("MOE Bmm1 Fused Gather": topk(logits, ..., apply_softmax=True), then the expert histogram
+ *  col_sum of the routing mask; "factor_moe_fused_gemm.cu": "factor 0", topk_softmax.)
+ * Up to 8192 slots (T * top_k) with E <= 1024 it is one launch from the logits to the
+ * alignment: the routing stays spread over the GPU (a wavefront per token), and the workgroup
+ * that finishes its routing last aligns every id.  The launch hands the ids from workgroup to
+ * workgroup through a completion counter, one of 64 that the library keeps per device and
+ * takes in turn per call, so at most 64 calls may be in flight at once across all streams of
+ * a device.  Larger problems run the routing launch and then the alignment launches on
+ * `stream`, with no host synchronisation between them.  Arguments and outputs are those of
+ * the two calls; results are identical to calling them in sequence.
  */
 int moe_route_align(const moe_problem* p, const float* logits, int renormalize,
                     int32_t* topk_ids, float* topk_weights, int32_t* counts, int32_t* offsets,

@@ -223,6 +223,13 @@ hipError_t launch_route_align(const Resolved& r, const float* logits, int renorm
 hipError_t launch_align(const Resolved& r, const int32_t* ids, int32_t* counts, int32_t* offsets,
                         int32_t* sorted_slots, int32_t* slot_row, int32_t* tiles,
                         int32_t* num_tiles, int32_t* n_invalid, hipStream_t s);
+// Routing and alignment as one launch (moe_align.hip), for the problems it covers.
+bool route_align_one_launch(const Resolved& r);
+hipError_t launch_route_align_one(const Resolved& r, const float* logits, int renorm,
+                                  int32_t* topk_ids, float* topk_w, int32_t* counts,
+                                  int32_t* offsets, int32_t* sorted_slots, int32_t* slot_row,
+                                  int32_t* tiles, int32_t* num_tiles, int32_t* n_invalid,
+                                  hipStream_t s);
 
 hipError_t launch_quant_rows(const Resolved& r, const void* x, uint8_t* xq, float* scales,
                              hipStream_t s);

@@ -43,16 +43,20 @@ hipError_t launch_route(const Resolved& r, const float* logits, int renorm, int3
   return hipGetLastError();
 }
 
-// Routing, then alignment of its ids: two launches on one stream, no host synchronisation.
-// Routing needs its waves spread over the GPU (a token's top-k is a chain of dependent
-// wavefront reductions, about 5 us per token), so a one-workgroup fusion with the alignment
-// is bound to one CU's latency; a fusion that keeps the routing spread has to hand the ids
-// across workgroups (a completion ticket with device-scope fences), and those fences, which
-// write back and invalidate the L2 of each of the 8 XCDs, cost more than the launch saved.
+// Routing, then alignment of its ids.  Up to kSmallN slots one launch does both
+// (route_align_kernel in moe_align.hip: routing spread over the GPU, the last workgroup to
+// finish aligns).  Above that the alignment itself needs several workgroups for its count and
+// placement, which wait on one another; handing work between them inside one launch (each
+// hand-over a device-scope counter that the waiting workgroups poll, then device-scope loads
+// of what the others wrote) was measured slower than the kernel boundaries, so larger
+// problems run the routing launch, then the alignment launches, on one stream.
 hipError_t launch_route_align(const Resolved& r, const float* logits, int renorm, int32_t* topk_ids,
                               float* topk_w, int32_t* counts, int32_t* offsets,
                               int32_t* sorted_slots, int32_t* slot_row, int32_t* tiles,
                               int32_t* num_tiles, int32_t* n_invalid, hipStream_t s) {
+  if (route_align_one_launch(r))
+    return launch_route_align_one(r, logits, renorm, topk_ids, topk_w, counts, offsets,
+                                  sorted_slots, slot_row, tiles, num_tiles, n_invalid, s);
   hipError_t e = launch_route(r, logits, renorm, topk_ids, topk_w, s);
   if (e != hipSuccess) return e;
   return launch_align(r, topk_ids, counts, offsets, sorted_slots, slot_row, tiles, num_tiles,

@@ -46,3 +46,42 @@ def test_forward_graph_replays_match_eager(device, name, kw):
         moe.forward(p, *args, out=out, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(out, eager)
+
+
+@pytest.mark.parametrize("T,E,k", [(64, 256, 8), (4096, 8, 2)])
+def test_route_align_graph_replays_match_eager(device, T, E, k):
+    """moe_route_align in one launch, captured: each replay reuses the completion counter taken
+    at capture (set back to zero by the launch's last workgroup), with eager calls, which take
+    other counters, between the replays."""
+    import numpy as np
+    rng = np.random.default_rng(8)
+    lg = torch.from_numpy(rng.standard_normal((T, E)).astype(np.float32)).to(device)
+    p = moe.make_problem(T, 128, 128, E, k, "bf16")
+    eager = moe.route_align(p, lg, True)
+    torch.cuda.synchronize()
+    b = {n: torch.empty_like(v) for n, v in eager.items()}
+
+    def call():
+        moe.moe_route_align(p, lg, True, b["topk_ids"], b["topk_weights"], b["counts"],
+                            b["offsets"], b["sorted_slots"], b["slot_row"], b["tiles"],
+                            b["num_tiles"], b["n_invalid"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(4):
+        for v in b.values():
+            v.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for n, v in eager.items():
+            assert torch.equal(b[n], v), f"replay {rep}: {n}"
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        for n, v in eager.items():
+            assert torch.equal(b[n], v), f"eager after replay {rep}: {n}"

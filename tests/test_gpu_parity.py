@@ -163,6 +163,54 @@ def test_route_and_route_align(device, name, lg, k, renorm):
     assert int(a["num_tiles"].item()) == o.num_tiles and int(a["n_invalid"].item()) == 0
 
 
+# moe_route_align in one launch (up to 8192 slots): the last workgroup to finish its routing
+# aligns the ids the others wrote.  Each call takes the next of the library's 64 completion
+# counters and the last workgroup sets it back to zero, so 70 calls in a row use every counter
+# and reuse some; calls on two streams at once use different counters.  Every call must equal
+# moe_route followed by moe_align, bit for bit, into buffers refilled with junk first.  The
+# 8194-slot case is just past the one-launch size (routing, then the alignment launches).
+ROUTE_ALIGN_REPEAT = [(64, 256, 8, True), (4096, 8, 2, True), (300, 16, 4, False),
+                      (1, 256, 8, True), (4097, 8, 2, True)]
+
+
+@pytest.mark.parametrize("T,E,k,renorm", ROUTE_ALIGN_REPEAT)
+def test_route_align_repeated_two_streams(device, T, E, k, renorm):
+    rng = np.random.default_rng([T, E, k])
+    lg = torch.from_numpy((rng.standard_normal((T, E)) * 2).astype(np.float32)).to(device)
+    p = moe.make_problem(T, 128, 128, E, k, "bf16")
+    say(f"route_align repeated T={T} E={E} k={k} N={T * k}")
+    ids, w = moe.route(p, lg, renorm)
+    ref = moe.align(p, ids)
+    torch.cuda.synchronize()
+    ref.update(topk_ids=ids, topk_weights=w)
+
+    def buffers():
+        b = moe.alloc_align(p, device)
+        b["topk_ids"] = torch.empty((T, k), dtype=torch.int32, device=device)
+        b["topk_weights"] = torch.empty((T, k), dtype=torch.float32, device=device)
+        return b
+
+    def call(b, stream):
+        for v in b.values():
+            v.fill_(-7 if v.dtype == torch.int32 else float("nan"))
+        moe.moe_route_align(p, lg, renorm, b["topk_ids"], b["topk_weights"], b["counts"],
+                            b["offsets"], b["sorted_slots"], b["slot_row"], b["tiles"],
+                            b["num_tiles"], b["n_invalid"], stream)
+
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    b1, b2 = buffers(), buffers()
+    torch.cuda.synchronize()
+    for it in range(35):
+        with torch.cuda.stream(s1):
+            call(b1, s1)
+        with torch.cuda.stream(s2):
+            call(b2, s2)
+        torch.cuda.synchronize()
+        for b in (b1, b2):
+            for key, v in ref.items():
+                assert torch.equal(b[key], v), f"call {it}: {key}"
+
+
 def test_align_deterministic_across_streams(device):
     cfg = CONFIGS["skewed_prefill_bf16"]
     from moe_inputs import make_routing
