@@ -23,10 +23,13 @@
 // offsets, tiles, padding) and place (one workgroup per chunk).  The per-chunk counts are
 // parked in the chunk's own part of slot_row, which only that chunk's place workgroup
 // overwrites, after reading them.
+//
+// moe_route_align's one-launch form (router producer, then this alignment) is here too:
+// route_align_kernel, below.
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
-#include <algorithm>
 #include "moe_route.h"
 
 
@@ -414,9 +417,10 @@ __global__ __launch_bounds__(kAlignThreads) void align_place_kernel(
 // the launch ends whatever the order and residency of its workgroups.
 //
 // Hand-over of the ids across the XCDs' L2 caches: they are written with device-scope stores
-// (write-through to memory), each wave waits for its stores to complete before the workgroup
+// (coherent across the XCDs), each wave waits for its stores to complete before the workgroup
 // barrier that precedes the ticket, the ticket is a device-scope atomic, and the aligning
-// workgroup reads the ids with device-scope loads, which miss any stale line of its own L2.
+// workgroup reads the ids with device-scope loads, which do not return a stale line of its
+// own XCD's L2.
 // A release/acquire pair on the ticket (a write-back of the whole L2 in every workgroup, an
 // invalidation in the last) gives the same result and was measured slower.
 //
