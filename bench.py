@@ -108,14 +108,15 @@ def blas_info():
     return "unknown", int(os.environ.get("OMP_NUM_THREADS", "1"))
 
 
-def cpu_baseline(case, n_tokens):
+def cpu_baseline(case, n_tokens, ids, w):
     """Time the CPU oracle (as it stands: float64 numpy, BLAS for the per-expert products) on the
-    first n_tokens tokens of the workload.  `cores` is the number of BLAS threads its products
-    run on (the rest of the oracle is single-threaded numpy)."""
+    first n_tokens tokens of the workload, routed by ids / w (host arrays [T, k]: the routing
+    the GPU step used).  `cores` is the number of BLAS threads its products run on (the rest of
+    the oracle is single-threaded numpy).  Returns (record, oracle output, tokens)."""
     import oracle
     cfg = case.cfg
     toks = list(range(min(n_tokens, cfg.T)))
-    needed = sorted(set(int(e) for e in case.ids_host[toks].reshape(-1) if 0 <= e < cfg.E))
+    needed = sorted(set(int(e) for e in ids[toks].reshape(-1) if 0 <= e < cfg.E))
     log(f"cpu_baseline: fetching {len(needed)} experts to the host")
     host = {e: case.expert_host(e) for e in needed}
     x = case.x_host()
@@ -124,17 +125,44 @@ def cpu_baseline(case, n_tokens):
     log(f"cpu_baseline: oracle on {len(toks)} tokens ({lib}, {threads} BLAS threads, "
         f"{visible} host cores visible)")
     t0 = time.perf_counter()
-    oracle.moe_layer(x, case.ids_host, case.w_host, lambda e: host[e], cfg.E,
-                     fp8=cfg.w_dtype == "e4m3", tokens=toks)
+    ref = oracle.moe_layer(x, ids, w, lambda e: host[e], cfg.E,
+                           fp8=cfg.w_dtype == "e4m3", tokens=toks)
     dt = time.perf_counter() - t0
     flops = 4 * len(toks) * cfg.top_k * cfg.H * cfg.I
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    res = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "seconds": round(dt, 3), "host_cores_visible": visible,
             "blas": {"library": lib, "threads": int(threads)}, "precision": "float64",
             "sample": f"first {len(toks)} of {cfg.T} tokens of {cfg.name} (all their experts), "
                       f"the float64 numpy oracle (per-expert products through BLAS on {threads} "
                       f"threads, the rest single-threaded), experts in sequence, weights "
                       f"prefetched to the host and not timed; useful flops 4*n*k*H*I"}
+    return res, ref, toks
+
+
+PARITY_TOL = {"f32": 1e-4, "bf16": 2e-2, "e4m3": 6e-2}   # max|gpu - oracle| / max|oracle|
+
+
+def parity_check(cfg, bm, out, a, ids, ref, toks):
+    """The layer output of the last timed step against the oracle output that cpu_baseline
+    computed from the same inputs and routing, and the step's alignment buffers `a` against the
+    oracle's alignment of the same ids, bit for bit."""
+    import numpy as np
+    import torch
+
+    import oracle
+    got = out[torch.tensor(toks, device=out.device)].float().cpu().numpy().astype(np.float64)
+    err = float(np.abs(got - ref).max() / np.abs(ref).max())
+    o = oracle.align(ids, cfg.E, bm)
+    exact = (a["counts"].cpu().numpy().tolist() == o.counts.tolist()
+             and a["offsets"].cpu().numpy().tolist() == o.offsets.tolist()
+             and np.array_equal(a["sorted_slots"].cpu().numpy(), o.sorted_slots)
+             and np.array_equal(a["slot_row"].cpu().numpy(), o.slot_row)
+             and np.array_equal(a["tiles"].cpu().numpy().reshape(-1, 2), o.tiles)
+             and int(a["num_tiles"].item()) == o.num_tiles)
+    tol = PARITY_TOL[cfg.w_dtype]
+    return {"max_rel_err": err, "tol": tol, "within_tol": err <= tol, "tokens_checked": len(toks),
+            "alignment_bit_exact": bool(exact),
+            "against": "the float64 oracle output of the cpu_baseline run, same inputs"}
 
 
 def dense_reference(args):
@@ -753,10 +781,19 @@ def run_workload(cfg, args, dev, cpu_on, block_m=0, routing=None):
         per_kernel[s] = d
 
     cpu = None
+    parity = None
     if cpu_on:
-        cpu = cpu_baseline(case, CPU_SAMPLE_TOKENS.get(cfg.name, 64))
+        torch.cuda.synchronize()
+        if routing:
+            ids_h, w_h = r_ids.cpu().numpy(), r_w.cpu().numpy().astype(np.float64)
+        else:
+            ids_h, w_h = case.ids_host, case.w_host
+        cpu, ref, toks = cpu_baseline(case, CPU_SAMPLE_TOKENS.get(cfg.name, 64), ids_h, w_h)
         if unit == "GB/s":
             cpu["note"] = "reported in TFLOP/s (useful flops); the GPU value is GB/s"
+        parity = parity_check(cfg, bm, out, a, ids_h, ref, toks)
+        log(f"parity: max|gpu-oracle|/max|oracle| = {parity['max_rel_err']:.3e} (tol {parity['tol']}), "
+            f"alignment bit-exact {parity['alignment_bit_exact']}")
 
     st = routing_stats(case.ids_host, cfg.E)
     res = {
@@ -787,6 +824,8 @@ def run_workload(cfg, args, dev, cpu_on, block_m=0, routing=None):
     }
     if routing_cmp:
         res["routing"] = routing_cmp
+    if parity:
+        res["parity"] = parity
     del case
     return res
 
