@@ -28,7 +28,9 @@ METRIC = "fused MoE layer useful TFLOP/s + % MFMA peak (prefill), HBM GB/s (deco
 PEAK_TFLOPS = {"bf16": 2516.6, "e4m3": 5033.2, "f32": 157.3}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "mixtral_prefill_bf16"
-EXTRA_KEY = {"dsv3_decode_bf16": "decode"}   # key of an extra workload's record
+# key of an extra workload's record, and the tokens its parity record checks against the oracle
+EXTRA_KEY = {"dsv3_decode_bf16": "decode", "skewed_prefill_bf16": "skewed", "dsv3_fp8_e4m3": "fp8"}
+EXTRA_PARITY_TOKENS = {"dsv3_decode_bf16": 8, "skewed_prefill_bf16": 256, "dsv3_fp8_e4m3": 8}
 CPU_SAMPLE_TOKENS = {"tiny_fp32": 16, "mixtral_prefill_bf16": 4096, "dsv3_decode_bf16": 16,
                      "skewed_prefill_bf16": 2048, "dsv3_fp8_e4m3": 64}
 
@@ -543,7 +545,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--block-m", type=int, default=0)
-    ap.add_argument("--extra-workloads", default="dsv3_decode_bf16",
+    ap.add_argument("--extra-workloads", default="dsv3_decode_bf16,skewed_prefill_bf16,dsv3_fp8_e4m3",
                     help="with the default workload: also time these workloads (comma list, or "
                          "'none') in the same process and add their records under their keys")
     ap.add_argument("--routing", choices=["on", "off"], default="off",
@@ -604,21 +606,26 @@ def main():
         # a second record in the same process, after the headline timing: its layer step, HBM
         # rate and the up GEMM's roofline; `value` stays the headline workload's
         torch.cuda.empty_cache()
-        r = run_workload(CONFIGS[name], args, dev, cpu_on=False, block_m=0, routing=False)
+        r = run_workload(CONFIGS[name], args, dev, cpu_on=False, block_m=0, routing=False,
+                         parity_tokens=EXTRA_PARITY_TOKENS.get(name, 8))
         res[EXTRA_KEY.get(name, name)] = {
-            k: r[k] for k in ("value", "unit", "ms_per_step", "ms_per_step_graph", "config",
-                              "layer_gbps_algorithmic", "kernels", "roofline")}
+            k: r.get(k) for k in ("value", "unit", "ms_per_step", "ms_per_step_graph", "config",
+                              "layer_gbps_algorithmic", "kernels", "roofline", "parity")}
         res[EXTRA_KEY.get(name, name)]["pct_hbm_peak_layer"] = round(
             100 * r["layer_gbps_algorithmic"] / PEAK_HBM_GBS, 2)
+        if "pct_mfma_peak_layer" in r:
+            res[EXTRA_KEY.get(name, name)]["pct_mfma_peak_layer"] = r["pct_mfma_peak_layer"]
         # the router producer on this workload's logits: one call against route, then align
         import routed_grouped_gemm_topk_amd as moe
         res[EXTRA_KEY.get(name, name)]["routing"] = routing_compare(moe, CONFIGS[name], dev)
     print(json.dumps(res), flush=True)
 
 
-def run_workload(cfg, args, dev, cpu_on, block_m=0, routing=None):
+def run_workload(cfg, args, dev, cpu_on, block_m=0, routing=None, parity_tokens=0):
     """Time one workload's step (staged entry points with HIP events, graph replay,
-    moe_forward) and return its result record."""
+    moe_forward) and return its result record.  cpu_on: time the oracle (cpu_baseline) and
+    check the step's output against it; else, with parity_tokens, only that check, on the first
+    parity_tokens tokens."""
     import numpy as np
     import torch
 
@@ -792,6 +799,11 @@ def run_workload(cfg, args, dev, cpu_on, block_m=0, routing=None):
         if unit == "GB/s":
             cpu["note"] = "reported in TFLOP/s (useful flops); the GPU value is GB/s"
         parity = parity_check(cfg, bm, out, a, ids_h, ref, toks)
+    elif parity_tokens:
+        torch.cuda.synchronize()
+        _, ref, toks = cpu_baseline(case, parity_tokens, case.ids_host, case.w_host)
+        parity = parity_check(cfg, bm, out, a, case.ids_host, ref, toks)
+    if parity:
         log(f"parity: max|gpu-oracle|/max|oracle| = {parity['max_rel_err']:.3e} (tol {parity['tol']}), "
             f"alignment bit-exact {parity['alignment_bit_exact']}")
 
